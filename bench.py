@@ -1,0 +1,300 @@
+"""Benchmark of the paged <-> Full Block KV-move path on one MI355X.
+
+One step = the layerwise loop of the Llama-3-8B-like workload (L=32, H_kv=8,
+d=128, bf16, B=16; 8 requests of T_hit=32768 hit and T_miss=512 miss tokens;
+24576-block pool, shuffled block tables): for every layer l, unpack_layer(l)
+of the hit slice into the paged slots, then merge_layer(l) of hit || miss into
+each request's complete_layer[l]; then pack_full of all T_all tokens of every
+request. All inputs are resident in HBM before timing.
+
+value = algorithmic bytes (read + write) of one step / step time, whole job.
+Also reported: each op's average launch time from HIP events on the launch
+stream, the roofline of the dominant kernel, a device copy ceiling, the
+small-object batched copy (200000 objects of 256*U{16..512} bytes) and the
+oracle timed on the host cores on one request of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-batch-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-batch-copy", action="store_true", help="skip the batched-copy section")
+    return ap.parse_args()
+
+
+class Events:
+    """Per-op launch timing with HIP events on the launch stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def around(self, name, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.setdefault(name, []).append((e0, e1))
+
+    def mean_ms(self, name):
+        return statistics.fmean(a.elapsed_time(b) for a, b in self.pairs[name])
+
+
+def llama_setup(torch, kv, wl, dev):
+    w = wl.LLAMA8B
+    sh = w.shape
+    L, S, B, rb, N = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, w.pool_blocks
+    C = sh.c_kv_bytes
+    R = len(w.t_hit)
+    t_hit, t_miss = w.t_hit[0], w.t_miss[0]
+    t_all = t_hit + t_miss
+    pool_bytes = L * S * N * B * rb
+    fb_bytes = t_hit * L * C
+    need = pool_bytes + R * (fb_bytes + t_miss * L * C + 2 * t_all * L * C)
+    free, _ = torch.cuda.mem_get_info(dev)
+    log(f"[bench] {w.name}: allocating {need / 2**30:.1f} GiB of {free / 2**30:.1f} GiB free")
+    if need > free:
+        raise SystemExit(f"workload needs {need} bytes, {free} free")
+    u8 = dict(dtype=torch.uint8, device=dev)
+    pool = torch.empty(pool_bytes, **u8)
+    wl.fill_bf16_normal_(pool, w.seed, 1)
+    tables = wl.block_tables(w.seed, 2, N, [wl.blocks_needed(t_all, B)] * R)
+    bts = [torch.from_numpy(t).to(dev) for t in tables]
+    fbs = [torch.empty(fb_bytes, **u8) for _ in range(R)]
+    misses = [torch.empty(t_miss * L * C, **u8) for _ in range(R)]
+    for r in range(R):
+        wl.fill_bf16_normal_(fbs[r], w.seed, 10 + r)
+        wl.fill_bf16_normal_(misses[r], w.seed, 30 + r)
+    complete = torch.empty(R * L * t_all * C, **u8)      # [R][L][T_all][C]
+    packed = [torch.empty(t_all * L * C, **u8) for _ in range(R)]
+    torch.cuda.synchronize()
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    unpack_seqs = [kv.seq(bts[r], fbs[r], t_hit) for r in range(R)]
+    pack_seqs = [kv.seq(bts[r], packed[r], t_all) for r in range(R)]
+    merge_by_layer = []
+    for l in range(L):
+        merge_by_layer.append([
+            kv.merge_seq(fbs[r].data_ptr() + l * C, L * C, t_hit,
+                         misses[r].data_ptr() + l * C, L * C, t_miss,
+                         complete.data_ptr() + (r * L + l) * t_all * C, C)
+            for r in range(R)])
+    bytes_unpack = 2 * R * t_hit * C
+    bytes_merge = 2 * R * t_all * C
+    bytes_pack = 2 * R * t_all * L * C
+    return dict(w=w, L=L, layout=layout, pool=pool, unpack_seqs=unpack_seqs, pack_seqs=pack_seqs,
+                merge_by_layer=merge_by_layer, C=C, keep=(bts, fbs, misses, complete, packed),
+                bytes=dict(unpack_layer=bytes_unpack, merge_layer=bytes_merge,
+                           pack_full=bytes_pack),
+                launches=dict(unpack_layer=L, merge_layer=L, pack_full=1))
+
+
+def llama_step(kv, ctx, s, ev=None):
+    L = s["L"]
+    for l in range(L):
+        if ev is None:
+            kv.kvm_unpack_layer(ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"])
+            kv.kvm_merge_layer(ctx.handle, s["C"], s["merge_by_layer"][l])
+        else:
+            ev.around("unpack_layer", lambda: kv.kvm_unpack_layer(
+                ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"]))
+            ev.around("merge_layer", lambda: kv.kvm_merge_layer(
+                ctx.handle, s["C"], s["merge_by_layer"][l]))
+    if ev is None:
+        kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, s["pack_seqs"])
+    else:
+        ev.around("pack_full", lambda: kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L,
+                                                        s["pack_seqs"]))
+
+
+def copy_ceiling(torch, dev, nbytes=2 << 30, reps=10):
+    """Device-to-device copy of nbytes through torch (hipMemcpy), read+write GB/s."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e6)
+
+
+def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
+    w = wl.SMALL_OBJS
+    descs_np = wl.small_object_descs(w)
+    total = int(descs_np[:, 2].sum())
+    log(f"[bench] {w.name}: {len(descs_np)} objects, {total / 1e9:.2f} GB each way")
+    u8 = dict(dtype=torch.uint8, device=dev)
+    src = torch.empty(w.src_arena, **u8)
+    wl.fill_random_bytes_(src, w.seed, 1)
+    dst = torch.empty(w.dst_arena, **u8)
+    descs = torch.from_numpy(descs_np.view(__import__("numpy").uint8).reshape(-1)).to(dev)
+    ctx.reserve(64, len(descs_np))
+    for _ in range(2):
+        kv.kvm_batch_copy(ctx.handle, dst, w.dst_arena, src, w.src_arena, descs, len(descs_np))
+    torch.cuda.synchronize()
+    ev = Events(torch)
+    for _ in range(reps):
+        ev.around("batch_copy", lambda: kv.kvm_batch_copy(ctx.handle, dst, w.dst_arena, src,
+                                                          w.src_arena, descs, len(descs_np)))
+    torch.cuda.synchronize()
+    ms = ev.mean_ms("batch_copy")
+    gbs = 2 * total / (ms * 1e6)
+    del src, dst, descs
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "objects": len(descs_np), "bytes_rw": 2 * total,
+            "ms_per_call": round(ms, 4), "GBps": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
+
+
+def cpu_baseline(wl, reps=3):
+    """The oracle on the host cores, on request 0 of the same workload: its 32
+    unpack_layer + merge_layer calls and its pack_full (1/8 of a step). The
+    request's 2080 blocks sit in a host pool of exactly that many blocks under
+    a random permutation table (the same random 32 KiB object accesses without
+    a 48 GiB host pool); every page is touched before timing."""
+    import numpy as np
+    import oracle
+    w = wl.LLAMA8B
+    sh = w.shape
+    L, S, B, rb = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes
+    C = sh.c_kv_bytes
+    t_hit, t_miss = w.t_hit[0], w.t_miss[0]
+    t_all = t_hit + t_miss
+    N = wl.blocks_needed(t_all, B)
+    table = wl.block_tables(w.seed, 2, N, [N])[0]
+    ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    pool = np.full(L * S * N * B * rb, 1, np.uint8)
+    fb = np.full(t_hit * L * C, 3, np.uint8)
+    miss = np.full(t_miss * L * C, 5, np.uint8)
+    complete = np.full(L * t_all * C, 7, np.uint8)
+    packed = np.full(t_all * L * C, 9, np.uint8)
+
+    def sample():
+        for l in range(L):
+            oracle.unpack_layer(pool, ref, L, l, table, t_hit, fb)
+            oracle.merge_layer(C, fb[l * C:], L * C, t_hit, miss[l * C:], L * C, t_miss,
+                               complete[l * t_all * C:], C)
+        oracle.pack_full(pool, ref, L, table, t_all, packed)
+
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        sample()
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
+    nbytes = L * 2 * t_hit * C + L * 2 * t_all * C + 2 * t_all * L * C
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"request 0 of 8 ({L} unpack_layer + {L} merge_layer + pack_full, "
+                      f"{nbytes / 1e9:.1f} GB), median of {reps} runs ({sum(times):.1f} s), "
+                      f"single thread, host pool of the request's {N} blocks"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards "
+              "by request with no exchange, so per-GPU throughput is the one-GPU figure",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_kvm_amd import kvmove as kv
+    from paged_kv_cache_kvm_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    kv.load()
+    ctx = kv.Context(0)
+
+    s = llama_setup(torch, kv, wl, dev)
+    step_bytes = sum(s["bytes"][k] * s["launches"][k] for k in s["bytes"])
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        llama_step(kv, ctx, s)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        llama_step(kv, ctx, s)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+    value = step_bytes * args.steps / dt / 1e9
+
+    # per-launch durations with HIP events on the launch stream
+    ev = Events(torch)
+    for _ in range(max(3, args.steps // 2)):
+        llama_step(kv, ctx, s, ev)
+    torch.cuda.synchronize()
+    ops = {}
+    for name in ("unpack_layer", "merge_layer", "pack_full"):
+        ms = ev.mean_ms(name)
+        gbs = s["bytes"][name] / (ms * 1e6)
+        ops[name] = {"launches_per_step": s["launches"][name],
+                     "bytes_per_launch": s["bytes"][name], "ms_per_launch": round(ms, 4),
+                     "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    dom = max(ops, key=lambda k: ops[k]["ms_per_launch"] * ops[k]["launches_per_step"])
+    assert ctx.take_device_errors() == 0
+    workload = s["w"].name
+    del s
+    torch.cuda.empty_cache()
+
+    ceiling = copy_ceiling(torch, dev)
+    bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
+    ctx.close()
+    cpu = None if args.no_cpu else cpu_baseline(wl)
+
+    kernel = {"unpack_layer": "k_unpack<16>", "merge_layer": "k_merge<16>",
+              "pack_full": "k_pack<16>"}[dom]
+    out = {
+        "metric": "effective KV-move GB/s (read+write) and % of HBM peak; descriptors/s",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": workload, "payload": "bf16 ~ N(0,1)", "layers": 32, "h_kv": 8,
+                   "head_dim": 128, "block_tokens": 16, "requests": 8, "t_hit": 32768,
+                   "t_miss": 512, "pool_blocks": 24576,
+                   "step": "32 x (unpack_layer + merge_layer) + pack_full",
+                   "bytes_per_step": step_bytes},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "ops": ops,
+        "roofline": {"bound": "hbm", "kernel": kernel, "op": dom,
+                     "achieved": ops[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ops[dom]["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+        "copy_ceiling_GBps": round(ceiling, 1),
+        "batch_copy": bc,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

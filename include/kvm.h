@@ -1,0 +1,231 @@
+/*
+ * kvm.h -- libkvmove: layerwise movement of KV-cache blocks between the paged
+ * HBM layout and the persistent cross-layer Full Block layout, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Four operations, each one stream-ordered launch:
+ *   kvm_pack_full     paged pool  -> Full Block [T][L][C_KV]       (all layers)
+ *   kvm_unpack_layer  Full Block layer slice -> paged slots          (one layer)
+ *   kvm_merge_layer   hit rows || miss rows -> complete_layer        (one layer)
+ *   kvm_batch_copy    many (src_off, dst_off, nbytes) objects        (one list)
+ *
+ * Sources (page title, section):
+ *   DualPath KV Loading, "Dual-Path Loading", key-objects table: the persisted
+ *     Full Block is a [T_hit, L, C_KV] view; hit_layer[l] is its layer-l slice
+ *     [T_hit, C_KV]; miss_layer[l] is [T_miss, C_KV]; complete_layer[l] is
+ *     [T_all, C_KV], the hit rows followed by the miss rows.
+ *   DualPath KV Loading, "two read paths": per layer the hit slice is written
+ *     into an HBM layer slot, and hit and miss are concatenated by token.
+ *   DualPath KV Loading, design checklist: the Full Block <-> layer-block
+ *     conversion keeps token, layer and KV-head order.
+ *   Tutti reading notes, prerequisites 3 (eq. 2): paged blocks of B_tokens
+ *     tokens, not contiguous, linked by a block table.
+ *   Tutti reading notes, prerequisites 5 (eq. 3-4) and design 1: one K and one
+ *     V object per layer per block; one compact (address, length) entry per
+ *     contiguous object; one launch per layer rather than one call per object
+ *     ("pseudo-code 1", layer-level batched retrieval).
+ *   Mooncake Ascend Transports, "why addresses need relocation": a transfer is
+ *     named by offsets from a known base, not by raw foreign pointers; and
+ *     "back to the real objects": an enqueued copy is not a finished copy.
+ *
+ * Conventions for every call
+ *   - Device pointers are HIP device addresses on the context's device. Host
+ *     arrays (kvm_seq, kvm_merge_seq) are read during the call and may be
+ *     reused as soon as it returns; the library stages what the kernels need.
+ *   - The caller owns every buffer and stream and keeps device buffers alive
+ *     until the stream has run the work. The library keeps no caller pointer
+ *     after a call returns.
+ *   - All operations are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream). KVM_OK means "enqueued"; the result is
+ *     there once the stream (or an event recorded after the call) completes.
+ *   - Every argument is validated before anything is enqueued: a call that
+ *     returns an error has enqueued nothing and written nothing.
+ *   - Payload is opaque bytes: no value is converted, so bf16 NaN payloads,
+ *     -0 and denormals move bit for bit.
+ *   - Any byte alignment is accepted. Pointers, strides and row sizes that are
+ *     all multiples of 16 bytes take 16-byte vector moves; otherwise the widest
+ *     unit dividing all of them is used.
+ *   - Device-side guards: a block-table entry outside [0, num_blocks) or a copy
+ *     object outside its buffer is skipped (its destination is left as it was)
+ *     and counted; kvm_take_device_errors() returns the count.
+ *   - One context per host thread; calls on one context are not thread-safe.
+ *   - Preconditions the library does not check: the block tables of one call
+ *     hold no repeated entry; pool rows described by the layout do not overlap;
+ *     copy destinations are pairwise disjoint and do not overlap the sources.
+ *     Violations give an unspecified (but in-bounds) result.
+ */
+#ifndef KVM_H
+#define KVM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVM_ABI_VERSION 1
+
+/* Status codes. */
+#define KVM_OK 0
+#define KVM_EINVAL (-1) /* null pointer, negative size or stride, malformed layout */
+#define KVM_ERANGE (-2) /* layer outside [0, L), a size above a supported limit   */
+#define KVM_ENOMEM (-3) /* device or pinned host memory could not be obtained      */
+#define KVM_EHIP (-4)   /* a HIP runtime call or launch failed; see kvm_ctx_last_error */
+
+typedef struct kvm_ctx kvm_ctx;
+
+/* Paged pool geometry (Tutti reading notes, prerequisites 3, eq. 2; one K and one
+ * V object per layer per block, prerequisites 5). The token row of
+ * (layer l, side s, block n, row r) starts at byte
+ *     l*layer_stride + s*side_stride + n*block_stride + r*row_bytes
+ * of the pool and is row_bytes long; the B rows of a block are contiguous.
+ * num_sides is 2 for separate K and V objects, 1 for a single latent (MLA).
+ * row_bytes is H_kv * head_dim * element size. layer_stride == 0 describes a
+ * one-layer slot pool that every layer reuses (DualPath's per-layer HBM slot).
+ * Requires num_sides >= 1, block_tokens >= 1, row_bytes >= 1, num_blocks >= 1,
+ * strides >= 0 and block_stride >= block_tokens*row_bytes when num_blocks > 1. */
+typedef struct {
+    int32_t num_sides;
+    int32_t block_tokens;
+    int64_t row_bytes;
+    int64_t block_stride;
+    int64_t side_stride;
+    int64_t layer_stride;
+    int64_t num_blocks;
+} kvm_pool_layout;
+
+/* One sequence for kvm_pack_full / kvm_unpack_layer.
+ *   block_table  device int32 array of at least ceil(num_tokens / block_tokens)
+ *                entries; token t lives in block block_table[t / B], row t % B.
+ *   full         device Full Block of this sequence, token-major
+ *                [T][L][num_sides * row_bytes] (DualPath key-objects table: the
+ *                [T, L, C_KV] view, C_KV = the K heads then the V heads). Token t,
+ *                layer l, side s starts at t*token_stride + (l*S + s)*row_bytes.
+ *   num_tokens   tokens to move: pack reads tokens [0, num_tokens) from the pool;
+ *                unpack writes tokens [0, num_tokens) (the hit tokens) into their
+ *                slots; every other slot byte is left as it was.
+ *   token_stride bytes between consecutive tokens of `full`; 0 means dense
+ *                (L * num_sides * row_bytes). Must be >= that dense size or 0. */
+typedef struct {
+    const int32_t* block_table;
+    void* full;
+    int64_t num_tokens;
+    int64_t token_stride;
+} kvm_seq;
+
+/* One request for kvm_merge_layer (DualPath "two read paths": the hit slice and
+ * the miss rows are concatenated by token). Rows are `row_bytes` long (C_KV
+ * bytes); strides are in bytes between consecutive rows.
+ *   hit   t_hit rows; hit + t*hit_stride. For the layer-l slice of a dense Full
+ *         Block pass full + l*C_KV bytes and hit_stride = L*C_KV bytes.
+ *   miss  t_miss rows; miss + i*miss_stride.
+ *   out   t_hit + t_miss rows: out + t*out_stride receives hit row t for
+ *         t < t_hit, and miss row t - t_hit after that. Row padding (bytes past
+ *         row_bytes within out_stride) is left as it was.
+ * A null pointer is allowed where its row count is 0. */
+typedef struct {
+    const void* hit;
+    int64_t hit_stride;
+    int64_t t_hit;
+    const void* miss;
+    int64_t miss_stride;
+    int64_t t_miss;
+    void* out;
+    int64_t out_stride;
+} kvm_merge_seq;
+
+/* One contiguous object of kvm_batch_copy: nbytes from src_base + src_off to
+ * dst_base + dst_off (Tutti reading notes, design 1, eq. 9: one entry per whole
+ * object; offsets relative to a known base as in Mooncake's relocation).
+ * 24 bytes; the array lives in DEVICE memory. */
+typedef struct {
+    uint64_t src_off;
+    uint64_t dst_off;
+    uint64_t nbytes;
+} kvm_copy_desc;
+
+/* KVM_ABI_VERSION of the built library. */
+int kvm_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char* kvm_strerror(int status);
+
+/* Create a context on HIP device `device`. It owns small device and pinned
+ * host staging buffers and a device error counter. *out is set only on
+ * KVM_OK. Errors: KVM_EINVAL (out NULL, device < 0), KVM_EHIP (no such
+ * device, runtime failure), KVM_ENOMEM. */
+int kvm_create(int device, kvm_ctx** out);
+
+/* Wait for the context's outstanding work, then free it. NULL is a no-op. */
+void kvm_destroy(kvm_ctx* ctx);
+
+/* Pre-size the context for up to max_seqs sequences per call and max_descs
+ * copy objects per call, so that later calls allocate nothing. Waits for the
+ * context's outstanding work if buffers must be replaced. A call larger than
+ * the reserve grows the buffers itself (synchronising the device once).
+ * Errors: KVM_EINVAL (negative sizes), KVM_ENOMEM, KVM_EHIP. */
+int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
+
+/* Text of the last HIP failure seen by this context ("" if none). */
+const char* kvm_ctx_last_error(const kvm_ctx* ctx);
+
+/* Synchronise the context's device, then return in *count the number of
+ * block-table entries and copy objects that device-side guards skipped since
+ * the previous call, and reset the counter. Errors: KVM_EINVAL, KVM_EHIP. */
+int kvm_take_device_errors(kvm_ctx* ctx, int64_t* count);
+
+/* Pack (DualPath key-objects table, the persisted Full Block): for each
+ * sequence, every token t < num_tokens, layer l < num_layers and side s:
+ *     full[t][l][s] <- pool[l][s][block_table[t / B]][t % B]        (row_bytes)
+ * One launch; one workgroup per (sequence, block, layer) tile.
+ * n == 0, or sequences with num_tokens == 0, enqueue nothing for them.
+ * Errors: KVM_EINVAL (null ctx/layout/pool/seqs with n > 0, a sequence with
+ * null pointers and num_tokens > 0, bad layout or strides, n < 0,
+ * num_layers < 1), KVM_ERANGE (n above 2^20, a tile above 2^31 bytes or
+ * 2^31 tiles), KVM_ENOMEM, KVM_EHIP. */
+int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
+                  int32_t num_layers, const kvm_seq* seqs, int32_t n, void* stream);
+
+/* Unpack one layer (DualPath "two read paths": the layer-l slice of the Full
+ * Block into the HBM layer slot): for each sequence, every token
+ * t < num_tokens and side s:
+ *     pool[layer][s][block_table[t / B]][t % B] <- full[t][layer][s]  (row_bytes)
+ * Slot rows of tokens >= num_tokens (a partial last block shared with miss
+ * tokens) are left as they were. One launch; one workgroup per
+ * (sequence, block) tile. Errors: as kvm_pack_full, plus KVM_ERANGE for
+ * layer outside [0, num_layers). */
+int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
+                     int32_t num_layers, int32_t layer, const kvm_seq* seqs, int32_t n,
+                     void* stream);
+
+/* Merge one layer (DualPath "two read paths": concatenate hit and miss by
+ * token into complete_layer[l] [T_all, C_KV]): for each request,
+ *     out row t      <- hit row t             for t < t_hit
+ *     out row t_hit+i <- miss row i           for i < t_miss
+ * One launch over all requests. Errors: KVM_EINVAL (null ctx, row_bytes < 1,
+ * negative counts or strides, a null pointer with a nonzero row count, n < 0),
+ * KVM_ERANGE (n above 2^20, row_bytes of 2^31 or more), KVM_ENOMEM, KVM_EHIP. */
+int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, int32_t n,
+                    void* stream);
+
+/* Batched copy of many small non-contiguous objects in one launch sequence
+ * (Tutti "pseudo-code 1": one submission per layer for thousands of objects;
+ * Mooncake Ascend Transports, USE_ASCEND: batching non-contiguous 128 KB blocks):
+ * for every k < n_descs,
+ *     dst_base[dst_off_k .. dst_off_k + nbytes_k) <- src_base[src_off_k .. + nbytes_k)
+ * descs is a DEVICE array of n_descs kvm_copy_desc. dst_bytes and src_bytes are
+ * the sizes of the two buffers; an object outside its buffer is skipped and
+ * counted (kvm_take_device_errors). Zero-length objects are no-ops. The bytes
+ * are split evenly over the device's wavefronts, so a few large objects and
+ * many small ones balance alike. dst_base and src_base may be the same
+ * buffer. Errors: KVM_EINVAL (null ctx, null descs/bases with n_descs > 0,
+ * n_descs < 0), KVM_ERANGE (n_descs above 2^32), KVM_ENOMEM, KVM_EHIP. */
+int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,
+                   uint64_t src_bytes, const kvm_copy_desc* descs, int64_t n_descs,
+                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVM_H */

@@ -1,0 +1,468 @@
+// kernels.hip -- gfx950 (CDNA4) kernels of libkvmove.
+//
+// Every kernel here is a byte mover: no value is read as a number. They are
+// bound by HBM bandwidth, so the design is about keeping enough 16-byte loads
+// in flight per CU, keeping every lane busy on ragged rows, and never writing
+// a partial cache line that a full row would cover:
+//
+//   k_pack / k_unpack   one workgroup per tile. A pack tile is (sequence,
+//                       block, layer); an unpack tile is (sequence, block).
+//                       A tile's rows (B tokens x sides) are flattened into
+//                       one index space of `unit`-byte elements so that a
+//                       1152-byte MLA row or a 256-byte tiny row keeps all 256
+//                       lanes busy; element -> (row, side, column) uses
+//                       multiply-high division by invariant integers.
+//   k_merge             one workgroup per (request, chunk of rows); a row comes
+//                       from the strided hit slice or from the miss rows.
+//   k_bc_*              batched copy: per-group byte sums (64 objects per
+//                       wavefront), one exclusive scan, then a fixed grid in
+//                       which every wavefront copies an equal share of the
+//                       total bytes, walking the objects its share covers.
+//
+// Page notation (DualPath KV Loading, key-objects table; Tutti reading notes,
+// prerequisites 3 and 5): T tokens, L layers, C_KV = sides * row_bytes per
+// token-layer row, B tokens per block, block table bt.
+#include "kvm_internal.h"
+
+namespace kvm {
+
+// Elements each thread keeps in flight between its loads and its stores.
+constexpr int kUnroll = 8;
+
+FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
+    f.s = l;
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
+{
+    const uint32_t hi = __umulhi(n, f.m);
+    return uint32_t((uint64_t(hi) + n) >> f.s);
+}
+
+template <int U> struct Unit;
+template <> struct Unit<16> { typedef uint32_t T __attribute__((ext_vector_type(4))); };
+template <> struct Unit<8> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
+template <> struct Unit<4> { typedef uint32_t T; };
+template <> struct Unit<2> { typedef uint16_t T; };
+template <> struct Unit<1> { typedef uint8_t T; };
+
+typedef Unit<16>::T V16;
+
+// Index of the record whose tile range holds `tile`: the last record whose
+// first tile is <= tile. tile0 is ascending with tile0[0] == 0 and every
+// record owns at least one tile. One coalesced load and a ballot per 64
+// records; the result is made wave-uniform so the record loads go through the
+// scalar cache.
+__device__ __forceinline__ int32_t find_record(const int64_t* __restrict__ tile0, int32_t n,
+                                               int64_t tile)
+{
+    const int lane = threadIdx.x & 63;
+    int32_t found = 0;
+    for (int32_t base = 0; base < n; base += 64) {
+        const int32_t i = base + lane;
+        const bool le = i < n && tile0[i] <= tile;
+        const int32_t c = __popcll(__ballot(le));
+        found = base + c - 1;
+        if (c < 64) break;
+    }
+    return __builtin_amdgcn_readfirstlane(found);
+}
+
+__device__ __forceinline__ bool bad_block(int32_t blk, int64_t num_blocks)
+{
+    return blk < 0 || int64_t(blk) >= num_blocks;
+}
+
+// ---------------------------------------------------------------- pack ---
+// full[t][l][s] <- pool[l][s][bt[t / B]][t % B] for the tokens of one block
+// and one layer. Element j of the tile: row r = j / (S*V), q = j % (S*V) is the
+// unit offset inside the token's C_KV row, side = q / V, column c = q % V.
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_pack(PoolGeom g, const char* __restrict__ pool,
+                                                 int32_t num_layers,
+                                                 const int64_t* __restrict__ tile0,
+                                                 const SeqRec* __restrict__ seqs, int32_t nseq,
+                                                 FastDiv div_q, FastDiv div_v,
+                                                 unsigned long long* err)
+{
+    typedef typename Unit<U>::T V;
+    const int64_t tile = blockIdx.x;
+    const int32_t si = find_record(tile0, nseq, tile);
+    const SeqRec s = seqs[si];
+    const int64_t rem = tile - tile0[si];
+    const int64_t b = rem / num_layers;
+    const int32_t l = int32_t(rem - b * num_layers);
+    const int32_t blk = s.block_table[b];
+    if (bad_block(blk, g.num_blocks)) {
+        if (threadIdx.x == 0) atomicAdd(err, 1ull);
+        return;
+    }
+    const int64_t t0 = b * g.block_tokens;
+    const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
+    const uint32_t total = rows * div_q.d;
+    const char* src = pool + l * g.layer_stride + blk * g.block_stride;
+    char* dst = const_cast<char*>(s.full) + t0 * s.token_stride + int64_t(l) * g.sides * g.row_bytes;
+
+    for (uint32_t base = threadIdx.x; base < total; base += kBlock * kUnroll) {
+        V v[kUnroll];
+        char* dp[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const uint32_t j = base + k * kBlock;
+            if (j < total) {
+                const uint32_t r = fdiv(j, div_q);
+                const uint32_t q = j - r * div_q.d;
+                const uint32_t side = fdiv(q, div_v);
+                const uint32_t c = q - side * div_v.d;
+                v[k] = *reinterpret_cast<const V*>(src + side * g.side_stride +
+                                                   int64_t(r) * g.row_bytes + int64_t(c) * U);
+                dp[k] = dst + int64_t(r) * s.token_stride + int64_t(q) * U;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const uint32_t j = base + k * kBlock;
+            if (j < total) *reinterpret_cast<V*>(dp[k]) = v[k];
+        }
+    }
+}
+
+// -------------------------------------------------------------- unpack ---
+// pool[layer][s][bt[t / B]][t % B] <- full[t][layer][s] for the tokens of one
+// block below num_tokens; same element order as k_pack.
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_unpack(PoolGeom g, char* __restrict__ pool,
+                                                   int32_t num_layers, int32_t layer,
+                                                   const int64_t* __restrict__ tile0,
+                                                   const SeqRec* __restrict__ seqs, int32_t nseq,
+                                                   FastDiv div_q, FastDiv div_v,
+                                                   unsigned long long* err)
+{
+    typedef typename Unit<U>::T V;
+    (void)num_layers;
+    const int64_t tile = blockIdx.x;
+    const int32_t si = find_record(tile0, nseq, tile);
+    const SeqRec s = seqs[si];
+    const int64_t b = tile - tile0[si];
+    const int32_t blk = s.block_table[b];
+    if (bad_block(blk, g.num_blocks)) {
+        if (threadIdx.x == 0) atomicAdd(err, 1ull);
+        return;
+    }
+    const int64_t t0 = b * g.block_tokens;
+    const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
+    const uint32_t total = rows * div_q.d;
+    const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
+    char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
+
+    for (uint32_t base = threadIdx.x; base < total; base += kBlock * kUnroll) {
+        V v[kUnroll];
+        char* dp[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const uint32_t j = base + k * kBlock;
+            if (j < total) {
+                const uint32_t r = fdiv(j, div_q);
+                const uint32_t q = j - r * div_q.d;
+                const uint32_t side = fdiv(q, div_v);
+                const uint32_t c = q - side * div_v.d;
+                v[k] = *reinterpret_cast<const V*>(src + int64_t(r) * s.token_stride +
+                                                   int64_t(q) * U);
+                dp[k] = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const uint32_t j = base + k * kBlock;
+            if (j < total) *reinterpret_cast<V*>(dp[k]) = v[k];
+        }
+    }
+}
+
+// --------------------------------------------------------------- merge ---
+// out row t <- hit row t (t < t_hit) or miss row t - t_hit, for one chunk of
+// rows_per_tile rows of one request. Element j: row r = j / V, column j % V.
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_merge(int32_t rows_per_tile,
+                                                  const int64_t* __restrict__ tile0,
+                                                  const MergeRec* __restrict__ seqs, int32_t nseq,
+                                                  FastDiv div_v)
+{
+    typedef typename Unit<U>::T V;
+    const int64_t tile = blockIdx.x;
+    const int32_t si = find_record(tile0, nseq, tile);
+    const MergeRec m = seqs[si];
+    const int64_t row0 = (tile - tile0[si]) * rows_per_tile;
+    const int64_t t_all = m.t_hit + m.t_miss;
+    const uint32_t rows = uint32_t(min(int64_t(rows_per_tile), t_all - row0));
+    const uint32_t total = rows * div_v.d;
+
+    for (uint32_t base = threadIdx.x; base < total; base += kBlock * kUnroll) {
+        V v[kUnroll];
+        char* dp[kUnroll];
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const uint32_t j = base + k * kBlock;
+            if (j < total) {
+                const uint32_t r = fdiv(j, div_v);
+                const uint32_t c = j - r * div_v.d;
+                const int64_t row = row0 + r;
+                const char* sp = row < m.t_hit ? m.hit + row * m.hit_stride
+                                               : m.miss + (row - m.t_hit) * m.miss_stride;
+                v[k] = *reinterpret_cast<const V*>(sp + int64_t(c) * U);
+                dp[k] = m.out + row * m.out_stride + int64_t(c) * U;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kUnroll; ++k) {
+            const uint32_t j = base + k * kBlock;
+            if (j < total) *reinterpret_cast<V*>(dp[k]) = v[k];
+        }
+    }
+}
+
+// ---------------------------------------------------------- batch copy ---
+
+// Bytes object k contributes: its length, or 0 when it does not lie inside
+// both buffers (then it is skipped everywhere).
+__device__ __forceinline__ uint64_t object_bytes(const CopyDesc& x, uint64_t src_bytes,
+                                                 uint64_t dst_bytes)
+{
+    const bool ok = x.src_off <= src_bytes && x.nbytes <= src_bytes - x.src_off &&
+                    x.dst_off <= dst_bytes && x.nbytes <= dst_bytes - x.dst_off;
+    return ok ? x.nbytes : 0;
+}
+
+// One wavefront per group of 64 objects: the group's byte count.
+__global__ __launch_bounds__(kBlock) void k_bc_group_sums(const CopyDesc* __restrict__ descs,
+                                                          int64_t n, uint64_t src_bytes,
+                                                          uint64_t dst_bytes,
+                                                          uint64_t* __restrict__ group_sum,
+                                                          int64_t ngroups,
+                                                          unsigned long long* err)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t grp = int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    if (grp >= ngroups) return;
+    const int64_t k = grp * kDescGroup + lane;
+    unsigned long long len = 0;
+    if (k < n) {
+        const CopyDesc x = descs[k];
+        len = object_bytes(x, src_bytes, dst_bytes);
+        if (len != x.nbytes) atomicAdd(err, 1ull);
+    }
+    for (int o = 32; o > 0; o >>= 1) len += __shfl_xor(len, o);
+    if (lane == 0) group_sum[grp] = len;
+}
+
+// One workgroup: group_base[i] = sum of group_sum[0..i), group_base[ng] = total.
+__global__ __launch_bounds__(1024) void k_bc_scan(const uint64_t* __restrict__ group_sum,
+                                                  uint64_t* __restrict__ group_base, int64_t ng)
+{
+    __shared__ unsigned long long wave_total[16];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t per = (ng + 1023) / 1024;
+    const int64_t a = min(ng, int64_t(tid) * per);
+    const int64_t b = min(ng, a + per);
+    unsigned long long local = 0;
+    for (int64_t i = a; i < b; ++i) local += group_sum[i];
+    unsigned long long x = local;  // inclusive scan across the wavefront
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_total[wid] = x;
+    __syncthreads();
+    unsigned long long before = 0;
+    for (int w = 0; w < wid; ++w) before += wave_total[w];
+    unsigned long long run = before + x - local;
+    for (int64_t i = a; i < b; ++i) {
+        group_base[i] = run;
+        run += group_sum[i];
+    }
+    if (tid == 1023) group_base[ng] = before + x;
+}
+
+// Copy `len` bytes with one wavefront. When source and destination agree
+// modulo 16 the body moves as 16-byte vectors, kUnroll per lane in flight;
+// when they agree modulo 4 as dwords; otherwise byte by byte.
+__device__ __forceinline__ void wave_copy(const char* __restrict__ s, char* __restrict__ d,
+                                          uint64_t len, int lane)
+{
+    const uintptr_t sa = uintptr_t(s), da = uintptr_t(d);
+    if (((sa ^ da) & 15) == 0) {
+        uint64_t head = (16 - (da & 15)) & 15;
+        if (head > len) head = len;
+        if (uint64_t(lane) < head) d[lane] = s[lane];
+        s += head;
+        d += head;
+        len -= head;
+        const uint64_t nv = len >> 4;
+        const V16* sv = reinterpret_cast<const V16*>(s);
+        V16* dv = reinterpret_cast<V16*>(d);
+        for (uint64_t base = lane; base < nv; base += 64 * kUnroll) {
+            V16 v[kUnroll];
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+                const uint64_t i = base + 64 * k;
+                if (i < nv) v[k] = sv[i];
+            }
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+                const uint64_t i = base + 64 * k;
+                if (i < nv) dv[i] = v[k];
+            }
+        }
+        const uint64_t done = nv << 4;
+        if (uint64_t(lane) < len - done) d[done + lane] = s[done + lane];
+    } else if (((sa ^ da) & 3) == 0) {
+        uint64_t head = (4 - (da & 3)) & 3;
+        if (head > len) head = len;
+        if (uint64_t(lane) < head) d[lane] = s[lane];
+        s += head;
+        d += head;
+        len -= head;
+        const uint64_t nw = len >> 2;
+        const uint32_t* sw = reinterpret_cast<const uint32_t*>(s);
+        uint32_t* dw = reinterpret_cast<uint32_t*>(d);
+        for (uint64_t i = lane; i < nw; i += 64) dw[i] = sw[i];
+        const uint64_t done = nw << 2;
+        if (uint64_t(lane) < len - done) d[done + lane] = s[done + lane];
+    } else {
+        for (uint64_t i = lane; i < len; i += 64) d[i] = s[i];
+    }
+}
+
+// Fixed grid; wavefront w copies bytes [w*Q, (w+1)*Q) of the concatenation of
+// all objects (Q = total / wavefronts, rounded up to 4 KiB). It finds the
+// object holding its first byte from the group prefix sums (a binary search
+// over groups, then a scan across the 64 lanes of that group), then walks the
+// objects in order until its share is done. An object larger than Q is split
+// across wavefronts; many small objects go to one wavefront.
+__global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__ descs, int64_t n,
+                                                    const char* __restrict__ src,
+                                                    uint64_t src_bytes, char* __restrict__ dst,
+                                                    uint64_t dst_bytes,
+                                                    const uint64_t* __restrict__ group_base,
+                                                    int64_t ngroups)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t total = group_base[ngroups];
+    const uint64_t nwaves = uint64_t(gridDim.x) * kWavesPerBlock;
+    const uint64_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    uint64_t share = (total + nwaves - 1) / nwaves;
+    share = (share + 4095) & ~uint64_t(4095);
+    const uint64_t r0 = w * share;
+    if (r0 >= total) return;
+    const uint64_t r1 = min(r0 + share, total);
+
+    // last group whose first byte is <= r0
+    int64_t lo = 0, hi = ngroups - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (group_base[mid] <= r0) lo = mid;
+        else hi = mid - 1;
+    }
+    const int64_t k = lo * kDescGroup + lane;
+    unsigned long long len = k < n ? object_bytes(descs[k], src_bytes, dst_bytes) : 0;
+    unsigned long long incl = len;
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const unsigned long long excl = incl - len;
+    const uint64_t rel = r0 - group_base[lo];
+    const uint64_t owner = __ballot(excl <= rel && rel < incl);
+    const int first = __ffsll((unsigned long long)owner) - 1;
+    int64_t kk = lo * kDescGroup + first;
+    uint64_t off = rel - __shfl(excl, first);
+
+    uint64_t pos = r0;
+    CopyDesc cur = descs[kk];
+    while (pos < r1) {
+        CopyDesc nxt = cur;
+        if (kk + 1 < n) nxt = descs[kk + 1];
+        const uint64_t clen = object_bytes(cur, src_bytes, dst_bytes);
+        const uint64_t take = min(clen - off, r1 - pos);
+        if (take) wave_copy(src + cur.src_off + off, dst + cur.dst_off + off, take, lane);
+        pos += take;
+        off = 0;
+        ++kk;
+        cur = nxt;
+    }
+}
+
+// ------------------------------------------------------------- launches ---
+
+#define KVM_UNIT_SWITCH(unit, CALL)                   \
+    switch (unit) {                                   \
+    case 16: CALL(16); break;                         \
+    case 8: CALL(8); break;                           \
+    case 4: CALL(4); break;                           \
+    case 2: CALL(2); break;                           \
+    default: CALL(1); break;                          \
+    }
+
+hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
+                       const int64_t* tile0, const SeqRec* seqs, int32_t nseq, int64_t ntiles,
+                       unsigned long long* err, hipStream_t st)
+{
+    const uint32_t v = uint32_t(g.row_bytes / unit);
+    const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
+#define KVM_PACK(U)                                                                         \
+    hipLaunchKernelGGL(k_pack<U>, dim3(uint32_t(ntiles)), dim3(kBlock), 0, st, g, pool,      \
+                       num_layers, tile0, seqs, nseq, dq, dv, err)
+    KVM_UNIT_SWITCH(unit, KVM_PACK)
+#undef KVM_PACK
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
+                         int32_t layer, const int64_t* tile0, const SeqRec* seqs, int32_t nseq,
+                         int64_t ntiles, unsigned long long* err, hipStream_t st)
+{
+    const uint32_t v = uint32_t(g.row_bytes / unit);
+    const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
+#define KVM_UNPACK(U)                                                                       \
+    hipLaunchKernelGGL(k_unpack<U>, dim3(uint32_t(ntiles)), dim3(kBlock), 0, st, g, pool,    \
+                       num_layers, layer, tile0, seqs, nseq, dq, dv, err)
+    KVM_UNIT_SWITCH(unit, KVM_UNPACK)
+#undef KVM_UNPACK
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const int64_t* tile0,
+                        const MergeRec* seqs, int32_t nseq, int64_t ntiles, hipStream_t st)
+{
+    const FastDiv dv = make_fastdiv(uint32_t(row_bytes / unit));
+#define KVM_MERGE(U)                                                                        \
+    hipLaunchKernelGGL(k_merge<U>, dim3(uint32_t(ntiles)), dim3(kBlock), 0, st, rows_per_tile, \
+                       tile0, seqs, nseq, dv)
+    KVM_UNIT_SWITCH(unit, KVM_MERGE)
+#undef KVM_MERGE
+    return hipGetLastError();
+}
+
+hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uint64_t src_bytes,
+                             const CopyDesc* descs, int64_t n, uint64_t* group_sum,
+                             uint64_t* group_base, int32_t copy_blocks, unsigned long long* err,
+                             hipStream_t st)
+{
+    const int64_t ng = (n + kDescGroup - 1) / kDescGroup;
+    const uint32_t sum_blocks = uint32_t((ng + kWavesPerBlock - 1) / kWavesPerBlock);
+    hipLaunchKernelGGL(k_bc_group_sums, dim3(sum_blocks), dim3(kBlock), 0, st, descs, n,
+                       src_bytes, dst_bytes, group_sum, ng, err);
+    hipLaunchKernelGGL(k_bc_scan, dim3(1), dim3(1024), 0, st, group_sum, group_base, ng);
+    hipLaunchKernelGGL(k_bc_copy, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs, n, src,
+                       src_bytes, dst, dst_bytes, group_base, ng);
+    return hipGetLastError();
+}
+
+}  // namespace kvm

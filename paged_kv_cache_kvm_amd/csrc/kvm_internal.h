@@ -1,0 +1,83 @@
+// kvm_internal.h -- records staged for the kernels and the launch entry points
+// shared by the C-ABI layer (api.cpp) and the gfx950 kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvm {
+
+// Workgroup size of the tile kernels and of the batched-copy kernel: four
+// wave64 wavefronts.
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / 64;
+
+// Copy objects are counted in groups of 64, one per lane of a wavefront.
+constexpr int kDescGroup = 64;
+
+// n / d for 32-bit n by one multiply-high, an add and a shift (division by an
+// invariant integer, Granlund and Montgomery 1994). d >= 1.
+struct FastDiv {
+    uint32_t d;
+    uint32_t m;
+    uint32_t s;
+};
+FastDiv make_fastdiv(uint32_t d);
+
+struct PoolGeom {
+    int32_t sides;
+    int32_t block_tokens;
+    int64_t row_bytes;
+    int64_t block_stride;
+    int64_t side_stride;
+    int64_t layer_stride;
+    int64_t num_blocks;
+};
+
+// Staged per sequence for pack/unpack. The tile index where each sequence
+// starts is staged separately as a dense int64 array in front of the records,
+// so a wavefront finds the sequence of a tile with one coalesced load.
+struct SeqRec {
+    const int32_t* block_table;
+    const char* full;
+    int64_t num_tokens;
+    int64_t token_stride;
+};
+
+struct MergeRec {
+    const char* hit;
+    int64_t hit_stride;
+    int64_t t_hit;
+    const char* miss;
+    int64_t miss_stride;
+    int64_t t_miss;
+    char* out;
+    int64_t out_stride;
+};
+
+struct CopyDesc {
+    uint64_t src_off;
+    uint64_t dst_off;
+    uint64_t nbytes;
+};
+
+// All launches go to `st` and return the launch status. `unit` is the move
+// width in bytes (16, 8, 4, 2 or 1) that divides every address and stride.
+hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
+                       const int64_t* tile0, const SeqRec* seqs, int32_t nseq, int64_t ntiles,
+                       unsigned long long* err, hipStream_t st);
+
+hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
+                         int32_t layer, const int64_t* tile0, const SeqRec* seqs, int32_t nseq,
+                         int64_t ntiles, unsigned long long* err, hipStream_t st);
+
+hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const int64_t* tile0,
+                        const MergeRec* seqs, int32_t nseq, int64_t ntiles, hipStream_t st);
+
+// group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1.
+hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uint64_t src_bytes,
+                             const CopyDesc* descs, int64_t n, uint64_t* group_sum,
+                             uint64_t* group_base, int32_t copy_blocks, unsigned long long* err,
+                             hipStream_t st);
+
+}  // namespace kvm

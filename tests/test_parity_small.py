@@ -1,0 +1,236 @@
+"""GPU parity at oracle-friendly sizes: every byte of every output of the HIP
+library (called through the C ABI) equals the oracle's on the same seeded
+inputs. Shapes span several tiles, ragged tails, every move width, every
+layout the pool descriptor allows, and the degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import SENTINEL, down, run_batch_copy, run_merge, run_pack_unpack, say, up
+from paged_kv_cache_kvm_amd import kvmove as kv
+from paged_kv_cache_kvm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx(gpu):
+    c = kv.Context(0)
+    yield c
+    c.close()
+
+
+def test_tiny_workload(ctx, gpu):
+    """The tiny workload end to end with its bf16 payload: pack_full(T_all),
+    unpack of the 240 hit tokens for every layer, merge for every layer."""
+    w = wl.TINY
+    sh = w.shape
+    L, S, B, rb, N = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, w.pool_blocks
+    C = sh.c_kv_bytes
+    t_hit, t_miss = w.t_hit[0], w.t_miss[0]
+    t_all = t_hit + t_miss
+    say(f"  tiny workload seed={w.seed}")
+    pool_np = wl.bf16_normal_bits(w.seed, 1, L * S * N * B * rb // 2).view(np.uint8)
+    bt_np = wl.block_tables(w.seed, 2, N, [wl.blocks_needed(t_all, B)])[0]
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    pool, bt = up(pool_np, gpu), up(bt_np, gpu)
+    full = torch.zeros(t_all * L * C, dtype=torch.uint8, device=gpu)
+    kv.kvm_pack_full(ctx.handle, layout, pool, L, [kv.seq(bt, full, t_all)])
+    full_ref = np.zeros(t_all * L * C, np.uint8)
+    oracle.pack_full(pool_np, ref, L, bt_np, t_all, full_ref)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(full), full_ref)
+
+    miss_np = wl.bf16_normal_bits(w.seed, 3, L * t_miss * C // 2).view(np.uint8)
+    miss = up(miss_np, gpu)
+    pool_b = up(np.full(pool_np.size, SENTINEL, np.uint8), gpu)
+    pool_b_ref = np.full(pool_np.size, SENTINEL, np.uint8)
+    for l in range(L):
+        kv.kvm_unpack_layer(ctx.handle, layout, pool_b, L, l, [kv.seq(bt, full, t_hit)])
+        oracle.unpack_layer(pool_b_ref, ref, L, l, bt_np, t_hit, full_ref)
+        out = torch.full((t_all * C,), SENTINEL, dtype=torch.uint8, device=gpu)
+        kv.kvm_merge_layer(ctx.handle, C, [kv.merge_seq(full.data_ptr() + l * C, L * C, t_hit,
+                                                        miss.data_ptr() + l * t_miss * C, C,
+                                                        t_miss, out, C)])
+        out_ref = np.full(t_all * C, SENTINEL, np.uint8)
+        oracle.merge_layer(C, full_ref[l * C:], L * C, t_hit, miss_np[l * t_miss * C:], C,
+                           t_miss, out_ref, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(out), out_ref), f"merge layer {l}"
+        assert np.array_equal(down(pool_b), pool_b_ref), f"unpack layer {l}"
+    assert ctx.take_device_errors() == 0
+
+
+PACK_CASES = [
+    # (L, S, N, B, rb, Ts, kind, block_pad, ts_pad, offset)
+    (4, 2, 64, 16, 256, [256], "dense", 0, 0, 0),
+    (4, 2, 64, 16, 256, [240, 17, 1], "dense", 0, 0, 0),
+    (3, 1, 300, 64, 1152, [700, 64, 65, 0, 1], "dense", 0, 0, 0),      # MLA-like rows
+    (2, 2, 40, 1, 2048, [33, 7], "dense", 0, 0, 0),                      # B = 1
+    (5, 2, 500, 3, 48, [2, 1] * 70, "dense", 0, 0, 0),                  # 140 sequences
+    (4, 2, 64, 16, 256, [200, 31], "block_major", 0, 0, 0),
+    (4, 2, 64, 16, 256, [200, 31], "slot", 0, 0, 0),
+    (3, 2, 50, 5, 80, [44, 13], "dense", 48, 96, 0),                     # padded blocks/tokens
+    (2, 2, 30, 4, 24, [23, 9], "dense", 8, 8, 8),                        # 8-byte moves
+    (2, 2, 30, 4, 12, [23, 9], "dense", 4, 4, 4),                        # 4-byte moves
+    (2, 2, 30, 4, 6, [23, 9], "dense", 2, 2, 2),                         # 2-byte moves
+    (2, 2, 30, 4, 5, [23, 9], "dense", 1, 3, 1),                         # byte moves
+    (2, 2, 64, 16, 256, [100, 50], "dense", 0, 0, 1),                    # odd base address
+    (1, 1, 8, 7, 16, [0, 0, 5], "slot", 0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", PACK_CASES, ids=[f"pack{i}" for i in range(len(PACK_CASES))])
+def test_pack_unpack(ctx, gpu, case):
+    L, S, N, B, rb, Ts, kind, bp, tp, off = case
+    run_pack_unpack(ctx, gpu, L, S, N, B, rb, Ts, kind=kind, block_pad=bp, ts_pad=tp, offset=off,
+                    seed=hash(str(case)) & 0xFFFF)
+
+
+MERGE_CASES = [
+    # (C, reqs, L, hit_pad, miss_pad, out_pad, offset)
+    (512, [(240, 16)], 4, 0, 0, 0, 0),
+    (4096, [(300, 20), (0, 9), (13, 0), (0, 0), (64, 64)], 32, 0, 0, 0, 0),
+    (1152, [(1000, 77)], 61, 0, 0, 128, 0),
+    (36, [(5, 3)] * 90, 3, 4, 12, 28, 0),                 # 90 requests, 4-byte moves
+    (10, [(17, 5), (1, 1)], 2, 2, 6, 2, 2),               # 2-byte moves
+    (7, [(9, 4)], 2, 1, 3, 5, 1),                         # byte moves
+    (65536 * 2, [(3, 2)], 2, 0, 0, 0, 0),                 # rows above the tile target
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=[f"merge{i}" for i in range(len(MERGE_CASES))])
+def test_merge(ctx, gpu, case):
+    C, reqs, L, hp, mp, op, off = case
+    run_merge(ctx, gpu, C, reqs, L=L, hit_pad=hp, miss_pad=mp, out_pad=op, offset=off,
+              seed=hash(str(case)) & 0xFFFF)
+
+
+def _descs(src_off, dst_off, lens):
+    cols = [np.array([int(v) for v in (c.tolist() if isinstance(c, np.ndarray) else c)],
+                     dtype=object).astype(np.uint64)
+            for c in (src_off, dst_off, lens)]
+    return np.stack(cols, axis=1)
+
+
+def test_batch_copy_random(ctx, gpu):
+    rng = np.random.default_rng(21)
+    lens = 256 * rng.integers(16, 512, endpoint=True, size=3000)
+    arena = int(lens.sum()) + (64 << 20)
+    d = _descs(wl.placements(21, 1, lens, arena), wl.placements(21, 2, lens, arena), lens)
+    run_batch_copy(ctx, gpu, rng.integers(0, 256, arena, dtype=np.uint8),
+                   np.full(arena, SENTINEL, np.uint8), d, label="4K-128K objects")
+
+
+def test_batch_copy_alignment_matrix(ctx, gpu):
+    """Every (src % 16, dst % 16) pair, with lengths 0..300 and one 1 MiB object."""
+    rng = np.random.default_rng(22)
+    rows, at_s, at_d = [], 0, 0
+    for sa in range(16):
+        for da in range(16):
+            for ln in (0, 1, 15, 16, 17, 63, 64, 255, 300, int(rng.integers(0, 301))):
+                s = at_s + sa
+                dd = at_d + da
+                rows.append((s, dd, ln))
+                at_s = (s + ln + 31) // 16 * 16
+                at_d = (dd + ln + 31) // 16 * 16
+    rows.append((at_s + 3, at_d + 3, 1 << 20))
+    rows.append((at_s + (1 << 20) + 64, at_d + (1 << 20) + 67, (1 << 20) + 5))
+    d = np.array(rows, np.uint64)
+    size = int(max(d[:, 0].max(), d[:, 1].max())) + (2 << 20) + 256
+    run_batch_copy(ctx, gpu, rng.integers(0, 256, size, dtype=np.uint8),
+                   np.full(size, SENTINEL, np.uint8), d, label="alignment matrix")
+
+
+def test_batch_copy_one_large_object(ctx, gpu):
+    """A 96 MiB object is split across many wavefronts."""
+    rng = np.random.default_rng(23)
+    n = 96 << 20
+    src = rng.integers(0, 256, n + 4096, dtype=np.uint8)
+    d = _descs([4096], [256], [n])
+    run_batch_copy(ctx, gpu, src, np.full(n + 512, SENTINEL, np.uint8), d, label="one large")
+
+
+def test_batch_copy_many_tiny_objects(ctx, gpu):
+    rng = np.random.default_rng(24)
+    lens = rng.integers(0, 65, size=100000)
+    arena = int(lens.sum()) + 200000
+    d = _descs(wl.placements(24, 1, lens, arena, 1), wl.placements(24, 2, lens, arena, 1), lens)
+    run_batch_copy(ctx, gpu, rng.integers(0, 256, arena, dtype=np.uint8),
+                   np.full(arena, SENTINEL, np.uint8), d, label="100k tiny")
+
+
+def test_batch_copy_same_buffer(ctx, gpu):
+    rng = np.random.default_rng(25)
+    buf = rng.integers(0, 256, 1 << 22, dtype=np.uint8)
+    lens = 64 * rng.integers(1, 100, size=200)
+    offs = wl.placements(25, 1, np.concatenate([lens, lens]), 1 << 22, 64)
+    d = _descs(offs[:200], offs[200:], lens)
+    run_batch_copy(ctx, gpu, buf, buf, d, same_buffer=True, label="same buffer")
+
+
+def test_batch_copy_skips_out_of_range(ctx, gpu):
+    rng = np.random.default_rng(26)
+    size = 1 << 20
+    d = _descs([0, 100, size - 10, 5, 2**63, 7000], [0, 5000, 20000, size - 3, 30000, 2**64 - 8],
+               [64, 300, 11, 4, 8, 9])
+    run_batch_copy(ctx, gpu, rng.integers(0, 256, size, dtype=np.uint8),
+                   np.full(size, SENTINEL, np.uint8), d, expect_skipped=4, label="out of range")
+
+
+def test_raw_bits_survive(ctx, gpu):
+    """bf16 NaN payloads, infinities, -0 and denormals come out bit-identical."""
+    specials = np.array([0x7FC1, 0xFFFF, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x807F, 0x7FBF],
+                        np.uint16)
+    L, S, N, B, hd = 2, 2, 8, 4, 32
+    rb = hd * 2
+    pool16 = np.resize(specials, L * S * N * B * hd)
+    pool_np = pool16.view(np.uint8)
+    bt_np = np.array([5, 2, 7], np.int32)
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    T = 11
+    pool, bt = up(pool_np, gpu), up(bt_np, gpu)
+    full = torch.zeros(T * L * S * rb, dtype=torch.uint8, device=gpu)
+    kv.kvm_pack_full(ctx.handle, layout, pool, L, [kv.seq(bt, full, T)])
+    want = np.zeros(T * L * S * rb, np.uint8)
+    oracle.pack_full(pool_np, ref, L, bt_np, T, want)
+    torch.cuda.synchronize()
+    got = down(full)
+    assert np.array_equal(got, want)
+    assert set(np.unique(got.view(np.uint16))) <= set(specials.tolist())
+    d = up(np.array([[0, 0, pool_np.size]], np.uint64).view(np.uint8), gpu)
+    dst = torch.zeros(pool_np.size, dtype=torch.uint8, device=gpu)
+    kv.kvm_batch_copy(ctx.handle, dst, pool_np.size, pool, pool_np.size, d, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(dst), pool_np)
+
+
+def test_repeated_and_changing_records(ctx, gpu):
+    """Back-to-back calls with identical records reuse staged records; a change
+    in any field (token count, pointer) must be seen by the next launch."""
+    L, S, N, B, rb = 3, 2, 32, 4, 64
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    rng = np.random.default_rng(27)
+    bt_np = wl.block_tables(27, 1, N, [8])[0]
+    bt = up(bt_np, gpu)
+    fb_np = [rng.integers(0, 256, 32 * L * S * rb, dtype=np.uint8) for _ in range(2)]
+    fbs = [up(f, gpu) for f in fb_np]
+    pool = up(np.full(L * S * N * B * rb, SENTINEL, np.uint8), gpu)
+    want = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
+    side = torch.cuda.Stream()
+    plan = [(0, 32, 0, None), (1, 32, 0, None), (1, 32, 1, None), (2, 5, 1, None), (2, 5, 1, side),
+            (0, 31, 0, side), (1, 32, 1, None), (2, 32, 0, None)]
+    for layer, T, which, stream in plan:
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+        kv.kvm_unpack_layer(ctx.handle, layout, pool, L, layer, [kv.seq(bt, fbs[which], T)],
+                            stream=stream)
+        if stream is not None:
+            torch.cuda.current_stream().wait_stream(stream)
+        oracle.unpack_layer(want, ref, L, layer, bt_np, T, fb_np[which])
+    torch.cuda.synchronize()
+    assert np.array_equal(down(pool), want)
