@@ -37,7 +37,7 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-batch-copy", action="store_true", help="skip the batched-copy section")
@@ -111,22 +111,12 @@ def llama_setup(torch, kv, wl, dev):
                 launches=dict(unpack_layer=L, merge_layer=L, pack_full=1))
 
 
-def llama_step(kv, ctx, s, ev=None):
+def llama_step(kv, ctx, s):
     L = s["L"]
     for l in range(L):
-        if ev is None:
-            kv.kvm_unpack_layer(ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"])
-            kv.kvm_merge_layer(ctx.handle, s["C"], s["merge_by_layer"][l])
-        else:
-            ev.around("unpack_layer", lambda: kv.kvm_unpack_layer(
-                ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"]))
-            ev.around("merge_layer", lambda: kv.kvm_merge_layer(
-                ctx.handle, s["C"], s["merge_by_layer"][l]))
-    if ev is None:
-        kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, s["pack_seqs"])
-    else:
-        ev.around("pack_full", lambda: kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L,
-                                                        s["pack_seqs"]))
+        kv.kvm_unpack_layer(ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"])
+        kv.kvm_merge_layer(ctx.handle, s["C"], s["merge_by_layer"][l])
+    kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, s["pack_seqs"])
 
 
 def copy_ceiling(torch, dev, nbytes=2 << 30, reps=10):
@@ -249,14 +239,21 @@ def main():
     ms_step = dt * 1e3 / args.steps
     value = step_bytes * args.steps / dt / 1e9
 
-    # per-launch durations with HIP events on the launch stream
+    # per-launch durations: HIP events on the launch stream around a loop of
+    # each op alone (its launches back to back), divided by the launch count
     ev = Events(torch)
+    L = s["L"]
     for _ in range(max(3, args.steps // 2)):
-        llama_step(kv, ctx, s, ev)
+        ev.around("unpack_layer", lambda: [kv.kvm_unpack_layer(
+            ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"]) for l in range(L)])
+        ev.around("merge_layer", lambda: [kv.kvm_merge_layer(
+            ctx.handle, s["C"], s["merge_by_layer"][l]) for l in range(L)])
+        ev.around("pack_full", lambda: kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L,
+                                                        s["pack_seqs"]))
     torch.cuda.synchronize()
     ops = {}
     for name in ("unpack_layer", "merge_layer", "pack_full"):
-        ms = ev.mean_ms(name)
+        ms = ev.mean_ms(name) / s["launches"][name]
         gbs = s["bytes"][name] / (ms * 1e6)
         ops[name] = {"launches_per_step": s["launches"][name],
                      "bytes_per_launch": s["bytes"][name], "ms_per_launch": round(ms, 4),

@@ -1,6 +1,6 @@
 // api.cpp -- the extern "C" boundary of libkvmove: argument validation,
-// per-call staging of the small per-sequence records, grid sizing and status
-// mapping. Every check runs before anything is enqueued, so a call that
+// per-launch record batches (passed to the kernels by value), grid sizing and
+// status mapping. Every check runs before anything is enqueued, so a call that
 // returns an error has no side effect.
 #include "kvm.h"
 #include "kvm_internal.h"
@@ -23,36 +23,14 @@ namespace {
 constexpr int64_t kMaxSeqs = int64_t(1) << 20;
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxDescs = int64_t(1) << 32;
-constexpr int kStageSlots = 32;
 // Target bytes per merge tile; rows per tile = max(1, this / row_bytes).
 constexpr int64_t kMergeTileBytes = 64 * 1024;
-
-// A pinned host ring and a device ring of equal slots. A call copies its
-// records into a host slot and enqueues one small host-to-device copy on the
-// caller's stream; an event recorded after the kernel marks when the slot may
-// be overwritten. A call whose records are byte-identical to a slot staged
-// earlier on the same stream reuses that slot without a copy: in a per-layer
-// loop the unpack records repeat every layer. Slots are replaced least
-// recently used first.
-struct Stage {
-    char* host = nullptr;
-    char* dev = nullptr;
-    size_t slot_bytes = 0;
-    uint64_t tick = 0;
-    hipEvent_t done[kStageSlots] = {};
-    bool busy[kStageSlots] = {};
-    bool valid[kStageSlots] = {};
-    uint64_t used[kStageSlots] = {};
-    hipStream_t stream[kStageSlots] = {};
-    std::vector<char> content[kStageSlots];
-};
 
 }  // namespace
 
 struct kvm_ctx {
     int device = 0;
     int num_cus = 0;
-    Stage stage;
     unsigned long long* d_err = nullptr;
     uint64_t* d_groups = nullptr;  // group sums, then group bases
     int64_t group_cap = 0;         // groups the scratch holds
@@ -89,109 +67,6 @@ int fail_hip(kvm_ctx* ctx, hipError_t e, const char* what)
 {
     if (ctx) ctx->last_error = std::string(what) + ": " + hipGetErrorString(e);
     return KVM_EHIP;
-}
-
-void stage_release(kvm_ctx* c)
-{
-    Stage& s = c->stage;
-    for (int i = 0; i < kStageSlots; ++i) {
-        if (s.done[i]) {
-            if (s.busy[i]) (void)hipEventSynchronize(s.done[i]);
-            (void)hipEventDestroy(s.done[i]);
-            s.done[i] = nullptr;
-        }
-        s.busy[i] = false;
-    }
-    if (s.host) (void)hipHostFree(s.host);
-    if (s.dev) (void)hipFree(s.dev);
-    s.host = nullptr;
-    s.dev = nullptr;
-    s.slot_bytes = 0;
-    for (int i = 0; i < kStageSlots; ++i) {
-        s.valid[i] = false;
-        s.used[i] = 0;
-        s.content[i].clear();
-    }
-}
-
-int stage_reserve(kvm_ctx* c, size_t slot_bytes)
-{
-    slot_bytes = (slot_bytes + 4095) & ~size_t(4095);
-    if (slot_bytes <= c->stage.slot_bytes) return KVM_OK;
-    stage_release(c);
-    Stage& s = c->stage;
-    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&s.host), slot_bytes * kStageSlots,
-                                 hipHostMallocDefault);
-    if (e != hipSuccess) {
-        s.host = nullptr;
-        c->last_error = std::string("hipHostMalloc: ") + hipGetErrorString(e);
-        return KVM_ENOMEM;
-    }
-    e = hipMalloc(reinterpret_cast<void**>(&s.dev), slot_bytes * kStageSlots);
-    if (e != hipSuccess) {
-        s.dev = nullptr;
-        stage_release(c);
-        c->last_error = std::string("hipMalloc: ") + hipGetErrorString(e);
-        return KVM_ENOMEM;
-    }
-    for (int i = 0; i < kStageSlots; ++i) {
-        e = hipEventCreateWithFlags(&s.done[i], hipEventDisableTiming);
-        if (e != hipSuccess) {
-            s.done[i] = nullptr;
-            stage_release(c);
-            return fail_hip(c, e, "hipEventCreateWithFlags");
-        }
-    }
-    s.slot_bytes = slot_bytes;
-    return KVM_OK;
-}
-
-// Put `len` bytes where the next kernel on `st` can read them; *slot is the
-// slot to mark once that kernel is enqueued.
-int stage_put(kvm_ctx* c, const void* bytes, size_t len, hipStream_t st, char** dptr, int* slot)
-{
-    int rc = stage_reserve(c, len);
-    if (rc != KVM_OK) return rc;
-    Stage& s = c->stage;
-    ++s.tick;
-    for (int k = 0; k < kStageSlots; ++k) {
-        if (s.valid[k] && s.stream[k] == st && s.content[k].size() == len &&
-            std::memcmp(s.content[k].data(), bytes, len) == 0) {
-            s.used[k] = s.tick;
-            *slot = k;
-            *dptr = s.dev + size_t(k) * s.slot_bytes;
-            return KVM_OK;
-        }
-    }
-    int i = 0;
-    for (int k = 1; k < kStageSlots; ++k)
-        if (s.used[k] < s.used[i]) i = k;
-    s.valid[i] = false;
-    if (s.busy[i]) {
-        hipError_t e = hipEventSynchronize(s.done[i]);
-        if (e != hipSuccess) return fail_hip(c, e, "hipEventSynchronize");
-        s.busy[i] = false;
-    }
-    char* h = s.host + size_t(i) * s.slot_bytes;
-    char* d = s.dev + size_t(i) * s.slot_bytes;
-    std::memcpy(h, bytes, len);
-    hipError_t e = hipMemcpyAsync(d, h, len, hipMemcpyHostToDevice, st);
-    if (e != hipSuccess) return fail_hip(c, e, "hipMemcpyAsync (records)");
-    s.content[i].assign(static_cast<const char*>(bytes), static_cast<const char*>(bytes) + len);
-    s.stream[i] = st;
-    s.used[i] = s.tick;
-    s.valid[i] = true;
-    *slot = i;
-    *dptr = d;
-    return KVM_OK;
-}
-
-int stage_mark(kvm_ctx* c, int slot, hipStream_t st)
-{
-    hipError_t e = hipEventRecord(c->stage.done[slot], st);
-    if (e != hipSuccess) return fail_hip(c, e, "hipEventRecord");
-    c->stage.busy[slot] = true;
-    return KVM_OK;
 }
 
 // Widest move unit (16, 8, 4, 2, 1 bytes) that divides every value OR-ed in.
@@ -232,13 +107,11 @@ PoolGeom geom_of(const kvm_pool_layout* p)
     return g;
 }
 
-// Records for pack/unpack: [tile0 array padded to 64 entries][SeqRec array].
+// The sequences of one call that own at least one tile, with their tile
+// counts, split into launch batches of at most kvm::kRecsPerLaunch.
 struct SeqPlan {
-    std::vector<char> bytes;
-    int32_t nrec = 0;
-    int64_t ntiles = 0;
+    std::vector<kvm::SeqBatch> batches;
     uint64_t align_bits = 0;
-    size_t rec_offset = 0;
 };
 
 int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs, int32_t n,
@@ -248,9 +121,6 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
     if (n > 0 && !seqs) return KVM_EINVAL;
     if (n > kMaxSeqs) return KVM_ERANGE;
     const int64_t dense = int64_t(num_layers) * p->num_sides * p->row_bytes;
-    std::vector<int64_t> tile0;
-    std::vector<SeqRec> recs;
-    int64_t tiles = 0;
     uint64_t bits = 0;
     for (int32_t i = 0; i < n; ++i) {
         const kvm_seq& s = seqs[i];
@@ -260,27 +130,23 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
         const int64_t ts = s.token_stride ? s.token_stride : dense;
         if (ts < dense) return KVM_EINVAL;
         const int64_t nb = (s.num_tokens + p->block_tokens - 1) / p->block_tokens;
-        const int64_t t = per_layer_tiles ? nb * num_layers : nb;
-        tile0.push_back(tiles);
-        tiles += t;
-        if (tiles > kMaxTiles) return KVM_ERANGE;
-        SeqRec r;
-        r.block_table = s.block_table;
-        r.full = static_cast<const char*>(s.full);
-        r.num_tokens = s.num_tokens;
-        r.token_stride = ts;
-        recs.push_back(r);
+        const int64_t tiles = per_layer_tiles ? nb * num_layers : nb;
+        if (plan->batches.empty() || plan->batches.back().n == kvm::kRecsPerLaunch) {
+            plan->batches.emplace_back();
+            kvm::SeqBatch& nb_ = plan->batches.back();
+            std::memset(&nb_, 0, sizeof(nb_));
+        }
+        kvm::SeqBatch& b = plan->batches.back();
+        if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
+        b.rec[b.n].block_table = s.block_table;
+        b.rec[b.n].full = static_cast<const char*>(s.full);
+        b.rec[b.n].num_tokens = s.num_tokens;
+        b.rec[b.n].token_stride = ts;
+        b.tile0[b.n + 1] = b.tile0[b.n] + tiles;
+        ++b.n;
         bits |= uint64_t(uintptr_t(s.full)) | uint64_t(ts);
     }
-    plan->nrec = int32_t(recs.size());
-    plan->ntiles = tiles;
     plan->align_bits = bits;
-    const size_t padded = (tile0.size() + 63) / 64 * 64;
-    plan->rec_offset = padded * sizeof(int64_t);
-    plan->bytes.assign(plan->rec_offset + recs.size() * sizeof(SeqRec), 0);
-    if (!tile0.empty()) std::memcpy(plan->bytes.data(), tile0.data(), tile0.size() * sizeof(int64_t));
-    if (!recs.empty())
-        std::memcpy(plan->bytes.data() + plan->rec_offset, recs.data(), recs.size() * sizeof(SeqRec));
     return KVM_OK;
 }
 
@@ -346,8 +212,7 @@ int kvm_create(int device, kvm_ctx** out)
         delete c;
         return KVM_EHIP;
     }
-    int rc = stage_reserve(c, 64 * 1024);
-    if (rc == KVM_OK) rc = grow_groups(c, 1024);
+    int rc = grow_groups(c, 1024);
     if (rc == KVM_OK && hipEventCreateWithFlags(&c->copy_done, hipEventDisableTiming) != hipSuccess) {
         c->copy_done = nullptr;
         rc = KVM_EHIP;
@@ -364,7 +229,6 @@ void kvm_destroy(kvm_ctx* ctx)
 {
     if (!ctx) return;
     DeviceGuard guard(ctx->device);
-    stage_release(ctx);
     (void)hipDeviceSynchronize();
     if (ctx->copy_done) (void)hipEventDestroy(ctx->copy_done);
     if (ctx->d_groups) (void)hipFree(ctx->d_groups);
@@ -378,9 +242,6 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs)
     if (max_seqs > kMaxSeqs || max_descs > kMaxDescs) return KVM_ERANGE;
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
-    const size_t per = std::max(sizeof(SeqRec), sizeof(MergeRec)) + sizeof(int64_t);
-    int rc = stage_reserve(ctx, size_t(max_seqs + 64) * per);
-    if (rc != KVM_OK) return rc;
     return grow_groups(ctx, (max_descs + kvm::kDescGroup - 1) / kvm::kDescGroup);
 }
 
@@ -413,7 +274,7 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
     SeqPlan plan;
     rc = plan_seqs(layout, num_layers, seqs, n, pack, &plan);
     if (rc != KVM_OK) return rc;
-    if (plan.ntiles == 0) return KVM_OK;
+    if (plan.batches.empty()) return KVM_OK;
     if (!pool) return KVM_EINVAL;
     const uint64_t bits = plan.align_bits | uint64_t(uintptr_t(pool)) | uint64_t(layout->row_bytes) |
                           uint64_t(layout->block_stride) | uint64_t(layout->side_stride) |
@@ -423,22 +284,18 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    char* d = nullptr;
-    int slot = 0;
-    rc = stage_put(ctx, plan.bytes.data(), plan.bytes.size(), st, &d, &slot);
-    if (rc != KVM_OK) return rc;
-    const int64_t* tile0 = reinterpret_cast<const int64_t*>(d);
-    const SeqRec* recs = reinterpret_cast<const SeqRec*>(d + plan.rec_offset);
     const PoolGeom g = geom_of(layout);
-    hipError_t e;
-    if (pack)
-        e = kvm::launch_pack(unit, g, static_cast<const char*>(pool), num_layers, tile0, recs,
-                             plan.nrec, plan.ntiles, ctx->d_err, st);
-    else
-        e = kvm::launch_unpack(unit, g, static_cast<char*>(const_cast<void*>(pool)), num_layers,
-                               layer, tile0, recs, plan.nrec, plan.ntiles, ctx->d_err, st);
-    if (e != hipSuccess) return fail_hip(ctx, e, pack ? "k_pack launch" : "k_unpack launch");
-    return stage_mark(ctx, slot, st);
+    for (const kvm::SeqBatch& b : plan.batches) {
+        hipError_t e;
+        if (pack)
+            e = kvm::launch_pack(unit, g, static_cast<const char*>(pool), num_layers, b, ctx->d_err,
+                                 st);
+        else
+            e = kvm::launch_unpack(unit, g, static_cast<char*>(const_cast<void*>(pool)), num_layers,
+                                   layer, b, ctx->d_err, st);
+        if (e != hipSuccess) return fail_hip(ctx, e, pack ? "k_pack launch" : "k_unpack launch");
+    }
+    return KVM_OK;
 }
 
 int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
@@ -460,9 +317,7 @@ int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, 
     if (n > 0 && !seqs) return KVM_EINVAL;
     if (n > kMaxSeqs || row_bytes > INT32_MAX) return KVM_ERANGE;
     const int32_t rows_per_tile = int32_t(std::max<int64_t>(1, kMergeTileBytes / row_bytes));
-    std::vector<int64_t> tile0;
-    std::vector<MergeRec> recs;
-    int64_t tiles = 0;
+    std::vector<kvm::MergeBatch> batches;
     uint64_t bits = uint64_t(row_bytes);
     for (int32_t i = 0; i < n; ++i) {
         const kvm_merge_seq& m = seqs[i];
@@ -473,10 +328,14 @@ int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, 
         const int64_t t_all = m.t_hit + m.t_miss;
         if (t_all == 0) continue;
         if (!m.out) return KVM_EINVAL;
-        tile0.push_back(tiles);
-        tiles += (t_all + rows_per_tile - 1) / rows_per_tile;
-        if (tiles > kMaxTiles) return KVM_ERANGE;
-        MergeRec r;
+        if (batches.empty() || batches.back().n == kvm::kRecsPerLaunch) {
+            batches.emplace_back();
+            std::memset(&batches.back(), 0, sizeof(kvm::MergeBatch));
+        }
+        kvm::MergeBatch& b = batches.back();
+        const int64_t tiles = (t_all + rows_per_tile - 1) / rows_per_tile;
+        if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
+        MergeRec& r = b.rec[b.n];
         r.hit = static_cast<const char*>(m.hit);
         r.hit_stride = m.hit_stride;
         r.t_hit = m.t_hit;
@@ -485,32 +344,23 @@ int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, 
         r.t_miss = m.t_miss;
         r.out = static_cast<char*>(m.out);
         r.out_stride = m.out_stride;
-        recs.push_back(r);
+        b.tile0[b.n + 1] = b.tile0[b.n] + tiles;
+        ++b.n;
         bits |= uint64_t(uintptr_t(m.out)) | uint64_t(m.out_stride);
         if (m.t_hit > 0) bits |= uint64_t(uintptr_t(m.hit)) | uint64_t(m.hit_stride);
         if (m.t_miss > 0) bits |= uint64_t(uintptr_t(m.miss)) | uint64_t(m.miss_stride);
     }
-    if (tiles == 0) return KVM_OK;
+    if (batches.empty()) return KVM_OK;
     const int unit = move_unit(bits);
-    const size_t padded = (tile0.size() + 63) / 64 * 64;
-    const size_t rec_off = padded * sizeof(int64_t);
-    std::vector<char> bytes(rec_off + recs.size() * sizeof(MergeRec), 0);
-    std::memcpy(bytes.data(), tile0.data(), tile0.size() * sizeof(int64_t));
-    std::memcpy(bytes.data() + rec_off, recs.data(), recs.size() * sizeof(MergeRec));
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    char* d = nullptr;
-    int slot = 0;
-    int rc = stage_put(ctx, bytes.data(), bytes.size(), st, &d, &slot);
-    if (rc != KVM_OK) return rc;
-    hipError_t e = kvm::launch_merge(unit, row_bytes, rows_per_tile,
-                                     reinterpret_cast<const int64_t*>(d),
-                                     reinterpret_cast<const MergeRec*>(d + rec_off),
-                                     int32_t(recs.size()), tiles, st);
-    if (e != hipSuccess) return fail_hip(ctx, e, "k_merge launch");
-    return stage_mark(ctx, slot, st);
+    for (const kvm::MergeBatch& b : batches) {
+        hipError_t e = kvm::launch_merge(unit, row_bytes, rows_per_tile, b, st);
+        if (e != hipSuccess) return fail_hip(ctx, e, "k_merge launch");
+    }
+    return KVM_OK;
 }
 
 int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,

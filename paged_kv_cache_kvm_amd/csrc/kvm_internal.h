@@ -34,9 +34,12 @@ struct PoolGeom {
     int64_t num_blocks;
 };
 
-// Staged per sequence for pack/unpack. The tile index where each sequence
-// starts is staged separately as a dense int64 array in front of the records,
-// so a wavefront finds the sequence of a tile with one coalesced load.
+// Per-call records travel to the kernels by value, as kernel arguments (no
+// host-to-device copy per call). A call with more than kRecsPerLaunch
+// sequences is split into several launches.
+constexpr int kRecsPerLaunch = 128;
+
+// One sequence of pack/unpack.
 struct SeqRec {
     const int32_t* block_table;
     const char* full;
@@ -44,6 +47,7 @@ struct SeqRec {
     int64_t token_stride;
 };
 
+// One request of merge.
 struct MergeRec {
     const char* hit;
     int64_t hit_stride;
@@ -55,6 +59,20 @@ struct MergeRec {
     int64_t out_stride;
 };
 
+// tile0[i] is the first tile of record i, ascending from 0; tile0[n] is the
+// launch's tile count. Every record owns at least one tile.
+struct SeqBatch {
+    int32_t n;
+    int64_t tile0[kRecsPerLaunch + 1];
+    SeqRec rec[kRecsPerLaunch];
+};
+
+struct MergeBatch {
+    int32_t n;
+    int64_t tile0[kRecsPerLaunch + 1];
+    MergeRec rec[kRecsPerLaunch];
+};
+
 struct CopyDesc {
     uint64_t src_off;
     uint64_t dst_off;
@@ -64,15 +82,14 @@ struct CopyDesc {
 // All launches go to `st` and return the launch status. `unit` is the move
 // width in bytes (16, 8, 4, 2 or 1) that divides every address and stride.
 hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
-                       const int64_t* tile0, const SeqRec* seqs, int32_t nseq, int64_t ntiles,
-                       unsigned long long* err, hipStream_t st);
+                       const SeqBatch& b, unsigned long long* err, hipStream_t st);
 
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
-                         int32_t layer, const int64_t* tile0, const SeqRec* seqs, int32_t nseq,
-                         int64_t ntiles, unsigned long long* err, hipStream_t st);
+                         int32_t layer, const SeqBatch& b, unsigned long long* err,
+                         hipStream_t st);
 
-hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const int64_t* tile0,
-                        const MergeRec* seqs, int32_t nseq, int64_t ntiles, hipStream_t st);
+hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
+                        hipStream_t st);
 
 // group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1.
 hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uint64_t src_bytes,
