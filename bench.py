@@ -209,6 +209,28 @@ def cpu_baseline(wl, reps=3):
                       f"single thread, host pool of the request's {N} blocks"}
 
 
+PROFILE = os.path.join(ROOT, "profiles", "llama8b_layer_loop_hbm_traffic.md")
+KERNEL_SOURCES = ("paged_kv_cache_kvm_amd/csrc/kernels.hip", "paged_kv_cache_kvm_amd/csrc/kvm_internal.h")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when that summary was taken on other kernel
+    sources than the ones built now."""
+    import hashlib
+    try:
+        line = next(l for l in open(PROFILE) if l.startswith("traffic-json: "))
+    except (OSError, StopIteration):
+        return None
+    rec = json.loads(line[len("traffic-json: "):])
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return rec["bytes_per_launch"].get(kernel)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -269,8 +291,7 @@ def main():
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
 
-    kernel = {"unpack_layer": "k_unpack<16>", "merge_layer": "k_merge<16>",
-              "pack_full": "k_pack<16>"}[dom]
+    kernel = {"unpack_layer": "k_unpack", "merge_layer": "k_merge", "pack_full": "k_pack"}[dom]
     out = {
         "metric": "effective KV-move GB/s (read+write) and % of HBM peak; descriptors/s",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -285,7 +306,9 @@ def main():
         "ops": ops,
         "roofline": {"bound": "hbm", "kernel": kernel, "op": dom,
                      "achieved": ops[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ops[dom]["GBps"] / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(ops[dom]["GBps"] / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(kernel),
+                     "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"]},
         "copy_ceiling_GBps": round(ceiling, 1),
         "batch_copy": bc,
         "cpu_baseline": cpu,

@@ -26,8 +26,8 @@
 
 namespace kvm {
 
-// Elements each thread keeps in flight between its loads and its stores.
-constexpr int kUnroll = 8;
+// 16-byte vectors each lane of a batched-copy wavefront keeps in flight.
+constexpr int kCopyUnroll = 8;
 
 FastDiv make_fastdiv(uint32_t d)
 {
@@ -97,17 +97,67 @@ __device__ __forceinline__ bool bad_block(int32_t blk, int64_t num_blocks)
     return blk < 0 || int64_t(blk) >= num_blocks;
 }
 
+// Copy the `total` unit-sized elements of one tile with a workgroup of BS
+// threads: every thread issues UNR loads, then UNR stores, so a workgroup keeps
+// BS*UNR*U bytes in flight. addr(j, src, dst) names element j's two addresses;
+// consecutive j are consecutive bytes of a token row, so a wavefront's 64 lanes
+// always touch 64 adjacent units. Which elements a wavefront takes per batch:
+//   WAVE_MAJOR = false: element k of thread t is base + k*BS + t (a wavefront's
+//                       UNR pieces are BS elements apart);
+//   WAVE_MAJOR = true:  each wavefront owns 64*UNR consecutive elements.
+template <int U, int BS, int UNR, bool WAVE_MAJOR, class Addr>
+__device__ __forceinline__ void copy_elements(uint32_t total, Addr addr)
+{
+    typedef typename Unit<U>::T V;
+    constexpr uint32_t kStep = WAVE_MAJOR ? 64 : BS;
+    const uint32_t first =
+        WAVE_MAJOR ? (threadIdx.x >> 6) * (64 * UNR) + (threadIdx.x & 63) : threadIdx.x;
+    // in wave-major order a wavefront's first element may exceed a thread's
+    // row of the batch, so iterate over whole batches
+    const uint32_t limit = WAVE_MAJOR ? total + BS * UNR : total;
+    for (uint32_t base = first; base < limit; base += BS * UNR) {
+        V v[UNR];
+        char* dp[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t j = base + k * kStep;
+            if (j < total) {
+                const char* sp;
+                addr(j, sp, dp[k]);
+                v[k] = ld(reinterpret_cast<const V*>(sp));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t j = base + k * kStep;
+            if (j < total) st(reinterpret_cast<V*>(dp[k]), v[k]);
+        }
+    }
+}
+
+// Workgroup shapes and element orders, chosen by measurement on MI355X (all
+// variants timed in one process on the same buffers, interleaved): pack and
+// merge keep a whole 64 KiB tile in flight per workgroup, pack in wave-major
+// order (+2.4 % over thread-major), merge in thread-major order (wave-major
+// costs it 18 %); unpack, whose stores land on scattered pool objects, does
+// best with half a tile in flight and no occupancy cap.
+constexpr int kPackBS = 1024, kPackUnroll = 4;
+constexpr bool kPackWaveMajor = true;
+constexpr int kMergeBS = 1024, kMergeUnroll = 4;
+constexpr bool kMergeWaveMajor = false;
+constexpr int kUnpackBS = 256, kUnpackUnroll = 8;
+constexpr bool kUnpackWaveMajor = false;
+
 // ---------------------------------------------------------------- pack ---
 // full[t][l][s] <- pool[l][s][bt[t / B]][t % B] for the tokens of one block
 // and one layer. Element j of the tile: row r = j / (S*V), q = j % (S*V) is the
 // unit offset inside the token's C_KV row, side = q / V, column c = q % V.
-template <int U>
-__global__ __launch_bounds__(kBlock) void k_pack(PoolGeom g, const char* __restrict__ pool,
-                                                 int32_t num_layers, const SeqBatch batch,
-                                                 FastDiv div_q, FastDiv div_v,
-                                                 unsigned long long* err)
+template <int U, int BS, int UNR, bool WM>
+__global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict__ pool,
+                                             int32_t num_layers, const SeqBatch batch,
+                                             FastDiv div_q, FastDiv div_v,
+                                             unsigned long long* err)
 {
-    typedef typename Unit<U>::T V;
     const int64_t tile = blockIdx.x;
     const int32_t si = find_record(batch.tile0, batch.n, tile);
     const SeqRec s = batch.rec[si];
@@ -121,44 +171,26 @@ __global__ __launch_bounds__(kBlock) void k_pack(PoolGeom g, const char* __restr
     }
     const int64_t t0 = b * g.block_tokens;
     const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-    const uint32_t total = rows * div_q.d;
     const char* src = pool + l * g.layer_stride + blk * g.block_stride;
     char* dst = const_cast<char*>(s.full) + t0 * s.token_stride + int64_t(l) * g.sides * g.row_bytes;
-
-    for (uint32_t base = threadIdx.x; base < total; base += kBlock * kUnroll) {
-        V v[kUnroll];
-        char* dp[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const uint32_t j = base + k * kBlock;
-            if (j < total) {
-                const uint32_t r = fdiv(j, div_q);
-                const uint32_t q = j - r * div_q.d;
-                const uint32_t side = fdiv(q, div_v);
-                const uint32_t c = q - side * div_v.d;
-                v[k] = ld(reinterpret_cast<const V*>(src + side * g.side_stride +
-                                                   int64_t(r) * g.row_bytes + int64_t(c) * U));
-                dp[k] = dst + int64_t(r) * s.token_stride + int64_t(q) * U;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const uint32_t j = base + k * kBlock;
-            if (j < total) st(reinterpret_cast<V*>(dp[k]), v[k]);
-        }
-    }
+    copy_elements<U, BS, UNR, WM>(rows * div_q.d, [&](uint32_t j, const char*& sp, char*& dp) {
+        const uint32_t r = fdiv(j, div_q);
+        const uint32_t q = j - r * div_q.d;
+        const uint32_t side = fdiv(q, div_v);
+        const uint32_t c = q - side * div_v.d;
+        sp = src + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+        dp = dst + int64_t(r) * s.token_stride + int64_t(q) * U;
+    });
 }
 
 // -------------------------------------------------------------- unpack ---
 // pool[layer][s][bt[t / B]][t % B] <- full[t][layer][s] for the tokens of one
 // block below num_tokens; same element order as k_pack.
-template <int U>
-__global__ __launch_bounds__(kBlock) void k_unpack(PoolGeom g, char* __restrict__ pool,
-                                                   int32_t layer, const SeqBatch batch,
-                                                   FastDiv div_q, FastDiv div_v,
-                                                   unsigned long long* err)
+template <int U, int BS, int UNR, bool WM>
+__global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ pool, int32_t layer,
+                                               const SeqBatch batch, FastDiv div_q, FastDiv div_v,
+                                               unsigned long long* err)
 {
-    typedef typename Unit<U>::T V;
     const int64_t tile = blockIdx.x;
     const int32_t si = find_record(batch.tile0, batch.n, tile);
     const SeqRec s = batch.rec[si];
@@ -170,72 +202,39 @@ __global__ __launch_bounds__(kBlock) void k_unpack(PoolGeom g, char* __restrict_
     }
     const int64_t t0 = b * g.block_tokens;
     const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-    const uint32_t total = rows * div_q.d;
     const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
     char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
-
-    for (uint32_t base = threadIdx.x; base < total; base += kBlock * kUnroll) {
-        V v[kUnroll];
-        char* dp[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const uint32_t j = base + k * kBlock;
-            if (j < total) {
-                const uint32_t r = fdiv(j, div_q);
-                const uint32_t q = j - r * div_q.d;
-                const uint32_t side = fdiv(q, div_v);
-                const uint32_t c = q - side * div_v.d;
-                v[k] = ld(reinterpret_cast<const V*>(src + int64_t(r) * s.token_stride +
-                                                   int64_t(q) * U));
-                dp[k] = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const uint32_t j = base + k * kBlock;
-            if (j < total) st(reinterpret_cast<V*>(dp[k]), v[k]);
-        }
-    }
+    copy_elements<U, BS, UNR, WM>(rows * div_q.d, [&](uint32_t j, const char*& sp, char*& dp) {
+        const uint32_t r = fdiv(j, div_q);
+        const uint32_t q = j - r * div_q.d;
+        const uint32_t side = fdiv(q, div_v);
+        const uint32_t c = q - side * div_v.d;
+        sp = src + int64_t(r) * s.token_stride + int64_t(q) * U;
+        dp = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+    });
 }
 
 // --------------------------------------------------------------- merge ---
 // out row t <- hit row t (t < t_hit) or miss row t - t_hit, for one chunk of
 // rows_per_tile rows of one request. Element j: row r = j / V, column j % V.
-template <int U>
-__global__ __launch_bounds__(kBlock) void k_merge(int32_t rows_per_tile, const MergeBatch batch,
-                                                  FastDiv div_v)
+template <int U, int BS, int UNR, bool WM>
+__global__ __launch_bounds__(BS) void k_merge(int32_t rows_per_tile, const MergeBatch batch,
+                                              FastDiv div_v)
 {
-    typedef typename Unit<U>::T V;
     const int64_t tile = blockIdx.x;
     const int32_t si = find_record(batch.tile0, batch.n, tile);
     const MergeRec m = batch.rec[si];
     const int64_t row0 = (tile - batch.tile0[si]) * rows_per_tile;
     const int64_t t_all = m.t_hit + m.t_miss;
     const uint32_t rows = uint32_t(min(int64_t(rows_per_tile), t_all - row0));
-    const uint32_t total = rows * div_v.d;
-
-    for (uint32_t base = threadIdx.x; base < total; base += kBlock * kUnroll) {
-        V v[kUnroll];
-        char* dp[kUnroll];
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const uint32_t j = base + k * kBlock;
-            if (j < total) {
-                const uint32_t r = fdiv(j, div_v);
-                const uint32_t c = j - r * div_v.d;
-                const int64_t row = row0 + r;
-                const char* sp = row < m.t_hit ? m.hit + row * m.hit_stride
-                                               : m.miss + (row - m.t_hit) * m.miss_stride;
-                v[k] = ld(reinterpret_cast<const V*>(sp + int64_t(c) * U));
-                dp[k] = m.out + row * m.out_stride + int64_t(c) * U;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kUnroll; ++k) {
-            const uint32_t j = base + k * kBlock;
-            if (j < total) st(reinterpret_cast<V*>(dp[k]), v[k]);
-        }
-    }
+    copy_elements<U, BS, UNR, WM>(rows * div_v.d, [&](uint32_t j, const char*& sp, char*& dp) {
+        const uint32_t r = fdiv(j, div_v);
+        const uint32_t c = j - r * div_v.d;
+        const int64_t row = row0 + r;
+        sp = (row < m.t_hit ? m.hit + row * m.hit_stride
+                            : m.miss + (row - m.t_hit) * m.miss_stride) + int64_t(c) * U;
+        dp = m.out + row * m.out_stride + int64_t(c) * U;
+    });
 }
 
 // ---------------------------------------------------------- batch copy ---
@@ -301,7 +300,7 @@ __global__ __launch_bounds__(1024) void k_bc_scan(const uint64_t* __restrict__ g
 }
 
 // Copy `len` bytes with one wavefront. When source and destination agree
-// modulo 16 the body moves as 16-byte vectors, kUnroll per lane in flight;
+// modulo 16 the body moves as 16-byte vectors, kCopyUnroll per lane in flight;
 // when they agree modulo 4 as dwords; otherwise byte by byte.
 __device__ __forceinline__ void wave_copy(const char* __restrict__ s, char* __restrict__ d,
                                           uint64_t len, int lane)
@@ -317,15 +316,15 @@ __device__ __forceinline__ void wave_copy(const char* __restrict__ s, char* __re
         const uint64_t nv = len >> 4;
         const V16* sv = reinterpret_cast<const V16*>(s);
         V16* dv = reinterpret_cast<V16*>(d);
-        for (uint64_t base = lane; base < nv; base += 64 * kUnroll) {
-            V16 v[kUnroll];
+        for (uint64_t base = lane; base < nv; base += 64 * kCopyUnroll) {
+            V16 v[kCopyUnroll];
 #pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
+            for (int k = 0; k < kCopyUnroll; ++k) {
                 const uint64_t i = base + 64 * k;
                 if (i < nv) v[k] = ld(sv + i);
             }
 #pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
+            for (int k = 0; k < kCopyUnroll; ++k) {
                 const uint64_t i = base + 64 * k;
                 if (i < nv) st(dv + i, v[k]);
             }
@@ -427,7 +426,7 @@ hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t nu
     const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
     const dim3 grid(uint32_t(b.tile0[b.n]));
 #define KVM_PACK(U)                                                                         \
-    hipLaunchKernelGGL(k_pack<U>, grid, dim3(kBlock), 0, st, g, pool, num_layers, b, dq, dv, err)
+    hipLaunchKernelGGL((k_pack<U, kPackBS, kPackUnroll, kPackWaveMajor>), grid, dim3(kPackBS), 0, st, g, pool, num_layers, b, dq, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_PACK)
 #undef KVM_PACK
     return hipGetLastError();
@@ -442,7 +441,7 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
     const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
     const dim3 grid(uint32_t(b.tile0[b.n]));
 #define KVM_UNPACK(U)                                                                       \
-    hipLaunchKernelGGL(k_unpack<U>, grid, dim3(kBlock), 0, st, g, pool, layer, b, dq, dv, err)
+    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, dq, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_UNPACK)
 #undef KVM_UNPACK
     return hipGetLastError();
@@ -454,7 +453,7 @@ hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, cons
     const FastDiv dv = make_fastdiv(uint32_t(row_bytes / unit));
     const dim3 grid(uint32_t(b.tile0[b.n]));
 #define KVM_MERGE(U)                                                                        \
-    hipLaunchKernelGGL(k_merge<U>, grid, dim3(kBlock), 0, st, rows_per_tile, b, dv)
+    hipLaunchKernelGGL((k_merge<U, kMergeBS, kMergeUnroll, kMergeWaveMajor>), grid, dim3(kMergeBS), 0, st, rows_per_tile, b, dv)
     KVM_UNIT_SWITCH(unit, KVM_MERGE)
 #undef KVM_MERGE
     return hipGetLastError();

@@ -7,8 +7,8 @@
 
 namespace kvm {
 
-// Workgroup size of the tile kernels and of the batched-copy kernel: four
-// wave64 wavefronts.
+// Workgroup size of the batched-copy kernels: four wave64 wavefronts. (The
+// tile kernels choose their own shapes in kernels.hip.)
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
 
