@@ -3,7 +3,7 @@
  * HBM layout and the persistent cross-layer Full Block layout, on one
  * AMD Instinct MI355X (gfx950).
  *
- * Four operations, each one stream-ordered launch:
+ * Four operations, each stream-ordered on the caller's stream:
  *   kvm_pack_full     paged pool  -> Full Block [T][L][C_KV]       (all layers)
  *   kvm_unpack_layer  Full Block layer slice -> paged slots          (one layer)
  *   kvm_merge_layer   hit rows || miss rows -> complete_layer        (one layer)
@@ -31,7 +31,8 @@
  * Conventions for every call
  *   - Device pointers are HIP device addresses on the context's device. Host
  *     arrays (kvm_seq, kvm_merge_seq) are read during the call and may be
- *     reused as soon as it returns; the library stages what the kernels need.
+ *     reused as soon as it returns: their contents travel to the kernels as
+ *     kernel arguments, up to 128 records per launch.
  *   - The caller owns every buffer and stream and keeps device buffers alive
  *     until the stream has run the work. The library keeps no caller pointer
  *     after a call returns.
@@ -150,34 +151,36 @@ int kvm_version(void);
 /* Static text for a status code. Never NULL. */
 const char* kvm_strerror(int status);
 
-/* Create a context on HIP device `device`. It owns small device and pinned
- * host staging buffers and a device error counter. *out is set only on
- * KVM_OK. Errors: KVM_EINVAL (out NULL, device < 0), KVM_EHIP (no such
- * device, runtime failure), KVM_ENOMEM. */
+/* Create a context on HIP device `device`. It owns a device error counter
+ * and the batched copy's scratch (two 64-bit words per 64 copy objects).
+ * *out is set only on KVM_OK. Errors: KVM_EINVAL (out NULL, device < 0),
+ * KVM_EHIP (no such device, runtime failure), KVM_ENOMEM. */
 int kvm_create(int device, kvm_ctx** out);
 
 /* Wait for the context's outstanding work, then free it. NULL is a no-op. */
 void kvm_destroy(kvm_ctx* ctx);
 
-/* Pre-size the context for up to max_seqs sequences per call and max_descs
- * copy objects per call, so that later calls allocate nothing. Waits for the
- * context's outstanding work if buffers must be replaced. A call larger than
- * the reserve grows the buffers itself (synchronising the device once).
- * Errors: KVM_EINVAL (negative sizes), KVM_ENOMEM, KVM_EHIP. */
+/* Pre-size the batched copy's scratch for up to max_descs copy objects per
+ * call, so that later calls allocate nothing. A call with more objects than
+ * the reserve grows the scratch itself (synchronising the device once).
+ * max_seqs, the sequences per call, needs no memory and is only range-checked
+ * (at most 2^20). Errors: KVM_EINVAL (negative sizes), KVM_ERANGE, KVM_ENOMEM,
+ * KVM_EHIP. */
 int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
 
 /* Text of the last HIP failure seen by this context ("" if none). */
 const char* kvm_ctx_last_error(const kvm_ctx* ctx);
 
 /* Synchronise the context's device, then return in *count the number of
- * block-table entries and copy objects that device-side guards skipped since
- * the previous call, and reset the counter. Errors: KVM_EINVAL, KVM_EHIP. */
+ * tiles (a block-table entry, per layer for pack) and copy objects that
+ * device-side guards skipped since the previous call, and reset the counter. Errors: KVM_EINVAL, KVM_EHIP. */
 int kvm_take_device_errors(kvm_ctx* ctx, int64_t* count);
 
 /* Pack (DualPath key-objects table, the persisted Full Block): for each
  * sequence, every token t < num_tokens, layer l < num_layers and side s:
  *     full[t][l][s] <- pool[l][s][block_table[t / B]][t % B]        (row_bytes)
- * One launch; one workgroup per (sequence, block, layer) tile.
+ * One launch per 128 sequences; one workgroup per (sequence, block, layer)
+ * tile.
  * n == 0, or sequences with num_tokens == 0, enqueue nothing for them.
  * Errors: KVM_EINVAL (null ctx/layout/pool/seqs with n > 0, a sequence with
  * null pointers and num_tokens > 0, bad layout or strides, n < 0,
@@ -191,8 +194,8 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  * t < num_tokens and side s:
  *     pool[layer][s][block_table[t / B]][t % B] <- full[t][layer][s]  (row_bytes)
  * Slot rows of tokens >= num_tokens (a partial last block shared with miss
- * tokens) are left as they were. One launch; one workgroup per
- * (sequence, block) tile. Errors: as kvm_pack_full, plus KVM_ERANGE for
+ * tokens) are left as they were. One launch per 128 sequences; one workgroup
+ * per (sequence, block) tile. Errors: as kvm_pack_full, plus KVM_ERANGE for
  * layer outside [0, num_layers). */
 int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
                      int32_t num_layers, int32_t layer, const kvm_seq* seqs, int32_t n,
@@ -202,7 +205,7 @@ int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
  * token into complete_layer[l] [T_all, C_KV]): for each request,
  *     out row t      <- hit row t             for t < t_hit
  *     out row t_hit+i <- miss row i           for i < t_miss
- * One launch over all requests. Errors: KVM_EINVAL (null ctx, row_bytes < 1,
+ * One launch per 128 requests. Errors: KVM_EINVAL (null ctx, row_bytes < 1,
  * negative counts or strides, a null pointer with a nonzero row count, n < 0),
  * KVM_ERANGE (n above 2^20, row_bytes of 2^31 or more), KVM_ENOMEM, KVM_EHIP. */
 int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, int32_t n,
