@@ -195,8 +195,12 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  *     pool[layer][s][block_table[t / B]][t % B] <- full[t][layer][s]  (row_bytes)
  * Slot rows of tokens >= num_tokens (a partial last block shared with miss
  * tokens) are left as they were. One launch per 128 sequences; one workgroup
- * per (sequence, block) tile. Errors: as kvm_pack_full, plus KVM_ERANGE for
- * layer outside [0, num_layers). */
+ * per (sequence, block) tile. Tiles run in ascending destination-block order:
+ * the first call with a given set of sequence records sorts them on the
+ * stream (a counting sort over the pool's blocks, kept in the context for the
+ * following layers; skipped when the pool has far more blocks than the call
+ * has tiles). Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
+ * [0, num_layers) or more than 2048 sequences with tokens in one call. */
 int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
                      int32_t num_layers, int32_t layer, const kvm_seq* seqs, int32_t n,
                      void* stream);

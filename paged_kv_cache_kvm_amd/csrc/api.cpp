@@ -26,6 +26,25 @@ constexpr int64_t kMaxDescs = int64_t(1) << 32;
 // Target bytes per merge tile; rows per tile = max(1, this / row_bytes).
 constexpr int64_t kMergeTileBytes = 64 * 1024;
 
+// Unpack tile orders (tiles sorted by destination block), one per distinct
+// launch batch, kept so that a per-layer loop sorts once. The key is the
+// batch's record bytes plus the pool's block count. A stale order (tables
+// rewritten in place under the same pointers) is still a permutation of the
+// same tiles, so results stay correct; only the write order is no longer
+// ascending.
+constexpr int kOrderSlots = 16;
+
+struct OrderSlot {
+    std::vector<char> key;
+    int32_t* order = nullptr;
+    int64_t cap = 0;
+    hipEvent_t ready = nullptr;     // after the sort kernels
+    hipEvent_t last_use = nullptr;  // after the latest unpack that read it
+    hipStream_t stream = nullptr;   // where the sort ran
+    uint64_t used = 0;
+    bool valid = false;
+};
+
 }  // namespace
 
 struct kvm_ctx {
@@ -39,6 +58,13 @@ struct kvm_ctx {
     hipEvent_t copy_done = nullptr;
     hipStream_t copy_stream = nullptr;
     bool copy_pending = false;
+    OrderSlot orders[kOrderSlots];
+    uint64_t order_tick = 0;
+    uint32_t* d_count = nullptr;   // counting-sort scratch, 2 * (blocks + 2) words
+    int64_t count_cap = 0;
+    hipEvent_t count_done = nullptr;
+    hipStream_t count_stream = nullptr;
+    bool count_pending = false;
     std::string last_error;
 };
 
@@ -150,6 +176,115 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
     return KVM_OK;
 }
 
+void order_release(kvm_ctx* c)
+{
+    for (OrderSlot& o : c->orders) {
+        if (o.order) (void)hipFree(o.order);
+        if (o.ready) (void)hipEventDestroy(o.ready);
+        if (o.last_use) (void)hipEventDestroy(o.last_use);
+        o = OrderSlot();
+    }
+    if (c->d_count) (void)hipFree(c->d_count);
+    if (c->count_done) (void)hipEventDestroy(c->count_done);
+    c->d_count = nullptr;
+    c->count_cap = 0;
+    c->count_done = nullptr;
+}
+
+std::vector<char> order_key(const kvm::SeqBatch& b, int64_t num_blocks)
+{
+    std::vector<char> k(sizeof(int64_t) * (b.n + 2) + sizeof(kvm::SeqRec) * b.n);
+    char* p = k.data();
+    std::memcpy(p, &num_blocks, sizeof(int64_t));
+    std::memcpy(p + sizeof(int64_t), b.tile0, sizeof(int64_t) * (b.n + 1));
+    std::memcpy(p + sizeof(int64_t) * (b.n + 2), b.rec, sizeof(kvm::SeqRec) * b.n);
+    return k;
+}
+
+// The unpack order of batch b, sorting it on `st` if it is not cached.
+// Device memory is obtained before anything is enqueued for this batch.
+int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStream_t st,
+                 OrderSlot** out)
+{
+    std::vector<char> key = order_key(b, num_blocks);
+    ++c->order_tick;
+    for (OrderSlot& o : c->orders) {
+        if (o.valid && o.key == key) {
+            if (o.stream != st) {
+                hipError_t e = hipStreamWaitEvent(st, o.ready, 0);
+                if (e != hipSuccess) return fail_hip(c, e, "hipStreamWaitEvent");
+            }
+            o.used = c->order_tick;
+            *out = &o;
+            return KVM_OK;
+        }
+    }
+    OrderSlot* o = &c->orders[0];
+    for (OrderSlot& x : c->orders)
+        if (x.used < o->used) o = &x;
+    if (o->valid) {  // its order may still be read by an unpack in flight
+        hipError_t e = hipEventSynchronize(o->last_use);
+        if (e != hipSuccess) return fail_hip(c, e, "hipEventSynchronize");
+        o->valid = false;
+    }
+    const int64_t ntiles = b.tile0[b.n];
+    hipError_t e;
+    if (!o->ready) {
+        if ((e = hipEventCreateWithFlags(&o->ready, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&o->last_use, hipEventDisableTiming)) != hipSuccess)
+            return fail_hip(c, e, "hipEventCreateWithFlags");
+    }
+    if (o->cap < ntiles) {
+        if (o->order) (void)hipFree(o->order);
+        o->order = nullptr;
+        o->cap = 0;
+        if (hipMalloc(reinterpret_cast<void**>(&o->order), size_t(ntiles) * sizeof(int32_t)) !=
+            hipSuccess) {
+            o->order = nullptr;
+            c->last_error = "hipMalloc: unpack order";
+            return KVM_ENOMEM;
+        }
+        o->cap = ntiles;
+    }
+    const int64_t words = 2 * (num_blocks + 2);
+    if (c->count_cap < words) {
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return fail_hip(c, e, "hipDeviceSynchronize");
+        if (c->d_count) (void)hipFree(c->d_count);
+        c->d_count = nullptr;
+        c->count_cap = 0;
+        c->count_pending = false;
+        if (hipMalloc(reinterpret_cast<void**>(&c->d_count), size_t(words) * sizeof(uint32_t)) !=
+            hipSuccess) {
+            c->d_count = nullptr;
+            c->last_error = "hipMalloc: unpack order scratch";
+            return KVM_ENOMEM;
+        }
+        c->count_cap = words;
+    }
+    if (!c->count_done &&
+        (e = hipEventCreateWithFlags(&c->count_done, hipEventDisableTiming)) != hipSuccess) {
+        c->count_done = nullptr;
+        return fail_hip(c, e, "hipEventCreateWithFlags");
+    }
+    if (c->count_pending && c->count_stream != st &&
+        (e = hipStreamWaitEvent(st, c->count_done, 0)) != hipSuccess)
+        return fail_hip(c, e, "hipStreamWaitEvent");
+    e = kvm::launch_unpack_order(b, num_blocks, c->d_count, o->order, st);
+    if (e != hipSuccess) return fail_hip(c, e, "unpack order launch");
+    if ((e = hipEventRecord(o->ready, st)) != hipSuccess ||
+        (e = hipEventRecord(c->count_done, st)) != hipSuccess)
+        return fail_hip(c, e, "hipEventRecord");
+    c->count_stream = st;
+    c->count_pending = true;
+    o->key = std::move(key);
+    o->stream = st;
+    o->used = c->order_tick;
+    o->valid = true;
+    *out = o;
+    return KVM_OK;
+}
+
 int grow_groups(kvm_ctx* c, int64_t groups)
 {
     if (groups <= c->group_cap) return KVM_OK;
@@ -230,6 +365,7 @@ void kvm_destroy(kvm_ctx* ctx)
     if (!ctx) return;
     DeviceGuard guard(ctx->device);
     (void)hipDeviceSynchronize();
+    order_release(ctx);
     if (ctx->copy_done) (void)hipEventDestroy(ctx->copy_done);
     if (ctx->d_groups) (void)hipFree(ctx->d_groups);
     if (ctx->d_err) (void)hipFree(ctx->d_err);
@@ -285,14 +421,33 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
     if (!guard.ok()) return KVM_EHIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const PoolGeom g = geom_of(layout);
-    for (const kvm::SeqBatch& b : plan.batches) {
+    std::vector<OrderSlot*> orders(plan.batches.size(), nullptr);
+    if (!pack) {
+        // Each batch holds its own cache slot for the whole call, so a call may
+        // have at most kOrderSlots batches. Sorting runs first, so that a
+        // failure leaves the caller's memory untouched (the sort kernels write
+        // only the context's own scratch). The counting sort costs O(blocks);
+        // for a pool much larger than the call's tiles the tiles keep their
+        // own order instead.
+        if (plan.batches.size() > size_t(kOrderSlots)) return KVM_ERANGE;
+        for (size_t i = 0; i < plan.batches.size(); ++i) {
+            const int64_t ntiles = plan.batches[i].tile0[plan.batches[i].n];
+            if (layout->num_blocks > 16 * ntiles + 65536) continue;
+            rc = unpack_order(ctx, plan.batches[i], layout->num_blocks, st, &orders[i]);
+            if (rc != KVM_OK) return rc;
+        }
+    }
+    for (size_t i = 0; i < plan.batches.size(); ++i) {
+        const kvm::SeqBatch& b = plan.batches[i];
         hipError_t e;
-        if (pack)
+        if (pack) {
             e = kvm::launch_pack(unit, g, static_cast<const char*>(pool), num_layers, b, ctx->d_err,
                                  st);
-        else
+        } else {
             e = kvm::launch_unpack(unit, g, static_cast<char*>(const_cast<void*>(pool)), num_layers,
-                                   layer, b, ctx->d_err, st);
+                                   layer, b, orders[i] ? orders[i]->order : nullptr, ctx->d_err, st);
+            if (e == hipSuccess && orders[i]) e = hipEventRecord(orders[i]->last_use, st);
+        }
         if (e != hipSuccess) return fail_hip(ctx, e, pack ? "k_pack launch" : "k_unpack launch");
     }
     return KVM_OK;

@@ -24,6 +24,8 @@
 // token-layer row, B tokens per block, block table bt.
 #include "kvm_internal.h"
 
+#include <algorithm>
+
 namespace kvm {
 
 // 16-byte vectors each lane of a batched-copy wavefront keeps in flight.
@@ -185,13 +187,17 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
 
 // -------------------------------------------------------------- unpack ---
 // pool[layer][s][bt[t / B]][t % B] <- full[t][layer][s] for the tokens of one
-// block below num_tokens; same element order as k_pack.
+// block below num_tokens; same element order as k_pack. Workgroup i takes tile
+// order[i]: the tiles sorted by destination block id (k_order_*), so the
+// object stores of concurrently running workgroups ascend through the pool
+// instead of landing at random. A null order keeps the tiles' own order.
 template <int U, int BS, int UNR, bool WM>
 __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ pool, int32_t layer,
-                                               const SeqBatch batch, FastDiv div_q, FastDiv div_v,
+                                               const SeqBatch batch, const int32_t* __restrict__ order,
+                                               FastDiv div_q, FastDiv div_v,
                                                unsigned long long* err)
 {
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = order ? order[blockIdx.x] : int64_t(blockIdx.x);
     const int32_t si = find_record(batch.tile0, batch.n, tile);
     const SeqRec s = batch.rec[si];
     const int64_t b = tile - batch.tile0[si];
@@ -237,6 +243,77 @@ __global__ __launch_bounds__(BS) void k_merge(int32_t rows_per_tile, const Merge
     });
 }
 
+// -------------------------------------------------- unpack tile order ---
+// A counting sort of one launch batch's unpack tiles by destination block id.
+// Measured on MI355X: writing the scattered 32 KiB pool objects in ascending
+// block order while the Full Block rows are read in whatever order that gives
+// is 6-7 % faster than the reverse. The sort is robust to any table contents:
+// an id outside [0, N) gets key N (its tile is skipped by k_unpack anyway),
+// and repeated ids share a key, so the result is always a permutation of the
+// batch's tiles.
+
+__device__ __forceinline__ int64_t order_key(const SeqRec& s, int64_t b, int64_t num_blocks)
+{
+    const int32_t blk = s.block_table[b];
+    return bad_block(blk, num_blocks) ? num_blocks : int64_t(blk);
+}
+
+__global__ __launch_bounds__(256) void k_order_zero(uint32_t* __restrict__ cnt, int64_t n)
+{
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+        cnt[i] = 0;
+}
+
+// grid: x = chunks of 256 tiles of one record, y = record
+__global__ __launch_bounds__(256) void k_order_count(const SeqBatch batch, int64_t num_blocks,
+                                                     uint32_t* __restrict__ cnt)
+{
+    const int32_t si = blockIdx.y;
+    const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (b >= batch.tile0[si + 1] - batch.tile0[si]) return;
+    atomicAdd(&cnt[order_key(batch.rec[si], b, num_blocks)], 1u);
+}
+
+__global__ __launch_bounds__(256) void k_order_place(const SeqBatch batch, int64_t num_blocks,
+                                                     uint32_t* __restrict__ cursor,
+                                                     int32_t* __restrict__ order)
+{
+    const int32_t si = blockIdx.y;
+    const int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (b >= batch.tile0[si + 1] - batch.tile0[si]) return;
+    const uint32_t pos = atomicAdd(&cursor[order_key(batch.rec[si], b, num_blocks)], 1u);
+    order[pos] = int32_t(batch.tile0[si] + b);
+}
+
+// One workgroup: out[i] = sum of in[0..i) for i < n, and out[n] = the total.
+template <class T>
+__global__ __launch_bounds__(1024) void k_exclusive_scan(const T* __restrict__ in,
+                                                         T* __restrict__ out, int64_t n)
+{
+    __shared__ T wave_total[16];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t a = min(n, int64_t(tid) * per);
+    const int64_t b = min(n, a + per);
+    T local = 0;
+    for (int64_t i = a; i < b; ++i) local += in[i];
+    T x = local;  // inclusive scan across the wavefront
+    for (int o = 1; o < 64; o <<= 1) {
+        const T y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_total[wid] = x;
+    __syncthreads();
+    T before = 0;
+    for (int w = 0; w < wid; ++w) before += wave_total[w];
+    T run = before + x - local;
+    for (int64_t i = a; i < b; ++i) {
+        out[i] = run;
+        run += in[i];
+    }
+    if (tid == 1023) out[n] = before + x;
+}
+
 // ---------------------------------------------------------- batch copy ---
 
 // Bytes object k contributes: its length, or 0 when it does not lie inside
@@ -269,34 +346,6 @@ __global__ __launch_bounds__(kBlock) void k_bc_group_sums(const CopyDesc* __rest
     }
     for (int o = 32; o > 0; o >>= 1) len += __shfl_xor(len, o);
     if (lane == 0) group_sum[grp] = len;
-}
-
-// One workgroup: group_base[i] = sum of group_sum[0..i), group_base[ng] = total.
-__global__ __launch_bounds__(1024) void k_bc_scan(const uint64_t* __restrict__ group_sum,
-                                                  uint64_t* __restrict__ group_base, int64_t ng)
-{
-    __shared__ unsigned long long wave_total[16];
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int64_t per = (ng + 1023) / 1024;
-    const int64_t a = min(ng, int64_t(tid) * per);
-    const int64_t b = min(ng, a + per);
-    unsigned long long local = 0;
-    for (int64_t i = a; i < b; ++i) local += group_sum[i];
-    unsigned long long x = local;  // inclusive scan across the wavefront
-    for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) wave_total[wid] = x;
-    __syncthreads();
-    unsigned long long before = 0;
-    for (int w = 0; w < wid; ++w) before += wave_total[w];
-    unsigned long long run = before + x - local;
-    for (int64_t i = a; i < b; ++i) {
-        group_base[i] = run;
-        run += group_sum[i];
-    }
-    if (tid == 1023) group_base[ng] = before + x;
 }
 
 // Copy `len` bytes with one wavefront. When source and destination agree
@@ -432,16 +481,33 @@ hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t nu
     return hipGetLastError();
 }
 
+hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* count_scratch,
+                               int32_t* order, hipStream_t st)
+{
+    int64_t most = 0;
+    for (int32_t i = 0; i < b.n; ++i) most = std::max<int64_t>(most, b.tile0[i + 1] - b.tile0[i]);
+    const int64_t keys = num_blocks + 1;
+    uint32_t* cnt = count_scratch;
+    uint32_t* cursor = count_scratch + keys;
+    const dim3 grid(uint32_t((most + 255) / 256), uint32_t(b.n));
+    hipLaunchKernelGGL(k_order_zero, dim3(uint32_t(std::min<int64_t>((keys + 255) / 256, 4096))),
+                       dim3(256), 0, st, cnt, keys);
+    hipLaunchKernelGGL(k_order_count, grid, dim3(256), 0, st, b, num_blocks, cnt);
+    hipLaunchKernelGGL(k_exclusive_scan<uint32_t>, dim3(1), dim3(1024), 0, st, cnt, cursor, keys);
+    hipLaunchKernelGGL(k_order_place, grid, dim3(256), 0, st, b, num_blocks, cursor, order);
+    return hipGetLastError();
+}
+
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
-                         int32_t layer, const SeqBatch& b, unsigned long long* err,
-                         hipStream_t st)
+                         int32_t layer, const SeqBatch& b, const int32_t* order,
+                         unsigned long long* err, hipStream_t st)
 {
     (void)num_layers;
     const uint32_t v = uint32_t(g.row_bytes / unit);
     const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
     const dim3 grid(uint32_t(b.tile0[b.n]));
 #define KVM_UNPACK(U)                                                                       \
-    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, dq, dv, err)
+    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dq, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_UNPACK)
 #undef KVM_UNPACK
     return hipGetLastError();
@@ -468,7 +534,9 @@ hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uin
     const uint32_t sum_blocks = uint32_t((ng + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL(k_bc_group_sums, dim3(sum_blocks), dim3(kBlock), 0, st, descs, n,
                        src_bytes, dst_bytes, group_sum, ng, err);
-    hipLaunchKernelGGL(k_bc_scan, dim3(1), dim3(1024), 0, st, group_sum, group_base, ng);
+    hipLaunchKernelGGL(k_exclusive_scan<unsigned long long>, dim3(1), dim3(1024), 0, st,
+                       reinterpret_cast<const unsigned long long*>(group_sum),
+                       reinterpret_cast<unsigned long long*>(group_base), ng);
     hipLaunchKernelGGL(k_bc_copy, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs, n, src,
                        src_bytes, dst, dst_bytes, group_base, ng);
     return hipGetLastError();

@@ -84,9 +84,16 @@ struct CopyDesc {
 hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
                        const SeqBatch& b, unsigned long long* err, hipStream_t st);
 
+// order: a permutation of the batch's tiles (workgroup i takes tile order[i]),
+// made by launch_unpack_order; null keeps the tiles' own order.
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
-                         int32_t layer, const SeqBatch& b, unsigned long long* err,
-                         hipStream_t st);
+                         int32_t layer, const SeqBatch& b, const int32_t* order,
+                         unsigned long long* err, hipStream_t st);
+
+// Sort the batch's unpack tiles by destination block id into `order`
+// (b.tile0[b.n] entries). count_scratch holds 2 * (num_blocks + 2) words.
+hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* count_scratch,
+                               int32_t* order, hipStream_t st);
 
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
                         hipStream_t st);

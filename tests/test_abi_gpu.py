@@ -89,6 +89,14 @@ def test_bad_arguments(ctx, bufs):
     assert np.all(down(pool) == SENTINEL), "a refused call wrote"
 
 
+def test_unpack_sequence_limit(ctx, bufs):
+    pool, bt, full = bufs
+    many = [kv.seq(bt, full, 1)] * 2049      # 17 launch batches of sequences with tokens
+    assert _status(kv.kvm_unpack_layer, ctx.handle, _layout(), pool, L, 0, many) == kv.KVM_ERANGE
+    torch.cuda.synchronize()
+    assert np.all(down(pool) == SENTINEL)
+
+
 def test_degenerate_calls_are_noops(ctx, bufs):
     pool, bt, full = bufs
     lay = _layout()

@@ -79,6 +79,7 @@ PACK_CASES = [
     (2, 2, 30, 4, 5, [23, 9], "dense", 1, 3, 1),                         # byte moves
     (2, 2, 64, 16, 256, [100, 50], "dense", 0, 0, 1),                    # odd base address
     (1, 1, 8, 7, 16, [0, 0, 5], "slot", 0, 0, 0),
+    (2, 2, 70000, 1, 16, [10, 3], "dense", 0, 0, 0),                    # pool >> tiles: own order
 ]
 
 
@@ -232,5 +233,49 @@ def test_repeated_and_changing_records(ctx, gpu):
         if stream is not None:
             torch.cuda.current_stream().wait_stream(stream)
         oracle.unpack_layer(want, ref, L, layer, bt_np, T, fb_np[which])
+    torch.cuda.synchronize()
+    assert np.array_equal(down(pool), want)
+
+
+def test_unpack_order_survives_table_rewrite(ctx, gpu):
+    """The unpack tile order is cached per record set. Rewriting a block table
+    in place (same pointer, same token count) leaves a stale order, which is
+    still a permutation of the same tiles: results must follow the new table."""
+    L, S, N, B, rb, T = 2, 2, 96, 4, 64, 90
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    rng = np.random.default_rng(31)
+    fb_np = rng.integers(0, 256, T * L * S * rb, dtype=np.uint8)
+    fb = up(fb_np, gpu)
+    tab1 = wl.block_tables(31, 1, N, [wl.blocks_needed(T, B)])[0]
+    tab2 = wl.block_tables(31, 2, N, [wl.blocks_needed(T, B)])[0]
+    bt = up(tab1, gpu)
+    want = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
+    pool = up(want, gpu)
+    for l, tab in ((0, tab1), (1, tab1), (0, tab2), (1, tab2)):
+        oracle.unpack_layer(want, ref, L, l, tab, T, fb_np)
+        bt.copy_(torch.from_numpy(tab.view(np.uint8)).to(gpu))   # in place, same pointer
+        kv.kvm_unpack_layer(ctx.handle, layout, pool, L, l, [kv.seq(bt, fb, T)])
+        torch.cuda.synchronize()
+        assert np.array_equal(down(pool), want), f"layer {l}"
+
+
+def test_unpack_order_cache_eviction(ctx, gpu):
+    """More distinct record sets than the context caches: evicted orders are
+    rebuilt and every call still matches the oracle."""
+    L, S, N, B, rb = 2, 2, 64, 4, 32
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    rng = np.random.default_rng(32)
+    fb_np = rng.integers(0, 256, 200 * L * S * rb, dtype=np.uint8)
+    fb = up(fb_np, gpu)
+    tab = wl.block_tables(32, 1, N, [50])[0]
+    bt = up(tab, gpu)
+    want = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
+    pool = up(want, gpu)
+    for i, T in enumerate(list(range(100, 140)) + list(range(100, 110))):   # 40 sets, then reuse
+        l = i % L
+        oracle.unpack_layer(want, ref, L, l, tab, T, fb_np)
+        kv.kvm_unpack_layer(ctx.handle, layout, pool, L, l, [kv.seq(bt, fb, T)])
     torch.cuda.synchronize()
     assert np.array_equal(down(pool), want)
