@@ -9,7 +9,8 @@ request. All inputs are resident in HBM before timing.
 
 value = algorithmic bytes (read + write) of one step / step time, whole job.
 Also reported: each op's average launch time from HIP events on the launch
-stream, the roofline of the dominant kernel, a device copy ceiling, the
+stream, the roofline of the dominant kernel, the same step with unpack and
+merge fused per layer (kvm_unpack_merge_layer), a device copy ceiling, the
 small-object batched copy (200000 objects of 256*U{16..512} bytes) and the
 oracle timed on the host cores on one request of the same workload.
 
@@ -101,11 +102,20 @@ def llama_setup(torch, kv, wl, dev):
                          misses[r].data_ptr() + l * C, L * C, t_miss,
                          complete.data_ptr() + (r * L + l) * t_all * C, C)
             for r in range(R)])
+    fused_by_layer = []
+    for l in range(L):
+        fused_by_layer.append([
+            kv.layer_seq(bts[r], fbs[r], t_hit, misses[r].data_ptr() + l * C, L * C, t_miss,
+                         complete.data_ptr() + (r * L + l) * t_all * C, C)
+            for r in range(R)])
     bytes_unpack = 2 * R * t_hit * C
     bytes_merge = 2 * R * t_all * C
     bytes_pack = 2 * R * t_all * L * C
+    # fused layer: read hit + miss once, write the pool slots and complete_layer
+    bytes_fused = R * C * (3 * t_hit + 2 * t_miss)
     return dict(w=w, L=L, layout=layout, pool=pool, unpack_seqs=unpack_seqs, pack_seqs=pack_seqs,
-                merge_by_layer=merge_by_layer, C=C, keep=(bts, fbs, misses, complete, packed),
+                merge_by_layer=merge_by_layer, fused_by_layer=fused_by_layer, bytes_fused=bytes_fused,
+                C=C, keep=(bts, fbs, misses, complete, packed),
                 bytes=dict(unpack_layer=bytes_unpack, merge_layer=bytes_merge,
                            pack_full=bytes_pack),
                 launches=dict(unpack_layer=L, merge_layer=L, pack_full=1))
@@ -117,6 +127,39 @@ def llama_step(kv, ctx, s):
         kv.kvm_unpack_layer(ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"])
         kv.kvm_merge_layer(ctx.handle, s["C"], s["merge_by_layer"][l])
     kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, s["pack_seqs"])
+
+
+def llama_fused_step(kv, ctx, s):
+    L = s["L"]
+    for l in range(L):
+        kv.kvm_unpack_merge_layer(ctx.handle, s["layout"], s["pool"], L, l, s["fused_by_layer"][l])
+    kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, s["pack_seqs"])
+
+
+def fused_section(torch, kv, ctx, s, steps, warmup, step_bytes, ms_separate):
+    """The same step with unpack_layer + merge_layer fused per layer."""
+    for _ in range(warmup):
+        llama_fused_step(kv, ctx, s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        llama_fused_step(kv, ctx, s)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev = Events(torch)
+    L = s["L"]
+    for _ in range(max(3, steps // 2)):
+        ev.around("fused", lambda: [kv.kvm_unpack_merge_layer(
+            ctx.handle, s["layout"], s["pool"], L, l, s["fused_by_layer"][l]) for l in range(L)])
+    torch.cuda.synchronize()
+    per = ev.mean_ms("fused") / L
+    gbs = s["bytes_fused"] / (per * 1e6)
+    return {"step": "32 x unpack_merge_layer + pack_full", "ms_per_step": round(ms, 3),
+            "speedup_vs_separate": round(ms_separate / ms, 3),
+            "effective_GBps": round(step_bytes / (ms * 1e6), 1),
+            "unpack_merge_layer": {"bytes_per_launch": s["bytes_fused"],
+                                   "ms_per_launch": round(per, 4), "GBps": round(gbs, 1),
+                                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}}
 
 
 def copy_ceiling(torch, dev, nbytes=2 << 30, reps=10):
@@ -281,6 +324,7 @@ def main():
                      "bytes_per_launch": s["bytes"][name], "ms_per_launch": round(ms, 4),
                      "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
     dom = max(ops, key=lambda k: ops[k]["ms_per_launch"] * ops[k]["launches_per_step"])
+    fused = fused_section(torch, kv, ctx, s, args.steps, args.warmup, step_bytes, ms_step)
     assert ctx.take_device_errors() == 0
     workload = s["w"].name
     del s
@@ -309,6 +353,7 @@ def main():
                      "frac": round(ops[dom]["GBps"] / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(kernel),
                      "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"]},
+        "fused_layer_loop": fused,
         "copy_ceiling_GBps": round(ceiling, 1),
         "batch_copy": bc,
         "cpu_baseline": cpu,

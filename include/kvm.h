@@ -8,6 +8,7 @@
  *   kvm_unpack_layer  Full Block layer slice -> paged slots          (one layer)
  *   kvm_merge_layer   hit rows || miss rows -> complete_layer        (one layer)
  *   kvm_batch_copy    many (src_off, dst_off, nbytes) objects        (one list)
+ * and kvm_unpack_merge_layer, unpack and merge of one layer in one pass.
  *
  * Sources (page title, section):
  *   DualPath KV Loading, "Dual-Path Loading", key-objects table: the persisted
@@ -214,6 +215,40 @@ int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
  * KVM_ERANGE (n above 2^20, row_bytes of 2^31 or more), KVM_ENOMEM, KVM_EHIP. */
 int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, int32_t n,
                     void* stream);
+
+/* One request for kvm_unpack_merge_layer: the union of its kvm_seq (the hit
+ * tokens of the Full Block and the block table) and its kvm_merge_seq (the
+ * miss rows and the complete_layer output). The hit rows are the layer slice
+ * of `full`, so there is no separate hit pointer.
+ *   block_table, full, t_hit, token_stride   as kvm_seq (num_tokens = t_hit)
+ *   miss, miss_stride, t_miss                 as kvm_merge_seq
+ *   out, out_stride                           as kvm_merge_seq (T_all rows) */
+typedef struct {
+    const int32_t* block_table;
+    const void* full;
+    int64_t t_hit;
+    int64_t token_stride;
+    const void* miss;
+    int64_t miss_stride;
+    int64_t t_miss;
+    void* out;
+    int64_t out_stride;
+} kvm_layer_seq;
+
+/* Unpack and merge one layer in one pass over the hit slice (DualPath "two
+ * read paths": the layer's hit slice goes both into the HBM layer slot and,
+ * concatenated with the miss rows, into complete_layer[l]). Exactly the result
+ * of kvm_unpack_layer(layer) on {block_table, full, t_hit, token_stride}
+ * followed by kvm_merge_layer(row_bytes = num_sides*row_bytes) on
+ * {hit = full + layer*num_sides*row_bytes, hit_stride = token_stride (dense if
+ * 0), t_hit, miss, miss_stride, t_miss, out, out_stride}, but each hit row is
+ * read once: 3*H + 2*M bytes move instead of 4*H + 2*M. Launches: one fused
+ * kernel per 128 requests for the hit rows (tiles in destination-block order,
+ * as kvm_unpack_layer) and one for the miss rows.
+ * Errors: the union of kvm_unpack_layer's and kvm_merge_layer's. */
+int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
+                           int32_t num_layers, int32_t layer, const kvm_layer_seq* seqs,
+                           int32_t n, void* stream);
 
 /* Batched copy of many small non-contiguous objects in one launch sequence
  * (Tutti "pseudo-code 1": one submission per layer for thousands of objects;

@@ -304,6 +304,58 @@ int grow_groups(kvm_ctx* c, int64_t groups)
     return KVM_OK;
 }
 
+// merge_layer records split into launch batches, with the widest move unit
+// that divides every pointer and stride seen.
+struct MergePlan {
+    explicit MergePlan(int64_t rb)
+        : row_bytes(rb), rows_per_tile(int32_t(std::max<int64_t>(1, kMergeTileBytes / rb))),
+          bits(uint64_t(rb))
+    {
+    }
+
+    int add(const void* hit, int64_t hit_stride, int64_t t_hit, const void* miss,
+            int64_t miss_stride, int64_t t_miss, void* out, int64_t out_stride)
+    {
+        if (t_hit < 0 || t_miss < 0 || hit_stride < 0 || miss_stride < 0 || out_stride < 0)
+            return KVM_EINVAL;
+        if ((t_hit > 0 && !hit) || (t_miss > 0 && !miss)) return KVM_EINVAL;
+        const int64_t t_all = t_hit + t_miss;
+        if (t_all == 0) return KVM_OK;
+        if (!out) return KVM_EINVAL;
+        if (batches.empty() || batches.back().n == kvm::kRecsPerLaunch) {
+            batches.emplace_back();
+            std::memset(&batches.back(), 0, sizeof(kvm::MergeBatch));
+        }
+        kvm::MergeBatch& b = batches.back();
+        const int64_t tiles = (t_all + rows_per_tile - 1) / rows_per_tile;
+        if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
+        b.rec[b.n] = {static_cast<const char*>(hit), hit_stride, t_hit,
+                      static_cast<const char*>(miss), miss_stride, t_miss,
+                      static_cast<char*>(out), out_stride};
+        b.tile0[b.n + 1] = b.tile0[b.n] + tiles;
+        ++b.n;
+        bits |= uint64_t(uintptr_t(out)) | uint64_t(out_stride);
+        if (t_hit > 0) bits |= uint64_t(uintptr_t(hit)) | uint64_t(hit_stride);
+        if (t_miss > 0) bits |= uint64_t(uintptr_t(miss)) | uint64_t(miss_stride);
+        return KVM_OK;
+    }
+
+    int launch(kvm_ctx* ctx, hipStream_t st) const
+    {
+        const int unit = move_unit(bits);
+        for (const kvm::MergeBatch& b : batches) {
+            hipError_t e = kvm::launch_merge(unit, row_bytes, rows_per_tile, b, st);
+            if (e != hipSuccess) return fail_hip(ctx, e, "k_merge launch");
+        }
+        return KVM_OK;
+    }
+
+    int64_t row_bytes;
+    int32_t rows_per_tile;
+    uint64_t bits;
+    std::vector<kvm::MergeBatch> batches;
+};
+
 }  // namespace
 
 extern "C" {
@@ -471,51 +523,97 @@ int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, 
     if (!ctx || row_bytes < 1 || n < 0) return KVM_EINVAL;
     if (n > 0 && !seqs) return KVM_EINVAL;
     if (n > kMaxSeqs || row_bytes > INT32_MAX) return KVM_ERANGE;
-    const int32_t rows_per_tile = int32_t(std::max<int64_t>(1, kMergeTileBytes / row_bytes));
-    std::vector<kvm::MergeBatch> batches;
-    uint64_t bits = uint64_t(row_bytes);
+    MergePlan plan(row_bytes);
     for (int32_t i = 0; i < n; ++i) {
         const kvm_merge_seq& m = seqs[i];
-        if (m.t_hit < 0 || m.t_miss < 0 || m.hit_stride < 0 || m.miss_stride < 0 ||
-            m.out_stride < 0)
-            return KVM_EINVAL;
-        if ((m.t_hit > 0 && !m.hit) || (m.t_miss > 0 && !m.miss)) return KVM_EINVAL;
-        const int64_t t_all = m.t_hit + m.t_miss;
-        if (t_all == 0) continue;
-        if (!m.out) return KVM_EINVAL;
-        if (batches.empty() || batches.back().n == kvm::kRecsPerLaunch) {
-            batches.emplace_back();
-            std::memset(&batches.back(), 0, sizeof(kvm::MergeBatch));
-        }
-        kvm::MergeBatch& b = batches.back();
-        const int64_t tiles = (t_all + rows_per_tile - 1) / rows_per_tile;
-        if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
-        MergeRec& r = b.rec[b.n];
-        r.hit = static_cast<const char*>(m.hit);
-        r.hit_stride = m.hit_stride;
-        r.t_hit = m.t_hit;
-        r.miss = static_cast<const char*>(m.miss);
-        r.miss_stride = m.miss_stride;
-        r.t_miss = m.t_miss;
-        r.out = static_cast<char*>(m.out);
-        r.out_stride = m.out_stride;
-        b.tile0[b.n + 1] = b.tile0[b.n] + tiles;
-        ++b.n;
-        bits |= uint64_t(uintptr_t(m.out)) | uint64_t(m.out_stride);
-        if (m.t_hit > 0) bits |= uint64_t(uintptr_t(m.hit)) | uint64_t(m.hit_stride);
-        if (m.t_miss > 0) bits |= uint64_t(uintptr_t(m.miss)) | uint64_t(m.miss_stride);
+        const int rc = plan.add(m.hit, m.hit_stride, m.t_hit, m.miss, m.miss_stride, m.t_miss,
+                                m.out, m.out_stride);
+        if (rc != KVM_OK) return rc;
     }
-    if (batches.empty()) return KVM_OK;
+    if (plan.batches.empty()) return KVM_OK;
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return KVM_EHIP;
+    return plan.launch(ctx, static_cast<hipStream_t>(stream));
+}
+
+int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
+                           int32_t num_layers, int32_t layer, const kvm_layer_seq* seqs, int32_t n,
+                           void* stream)
+{
+    if (!ctx) return KVM_EINVAL;
+    int rc = check_layout(layout, num_layers);
+    if (rc != KVM_OK) return rc;
+    if (layer < 0 || layer >= num_layers) return KVM_ERANGE;
+    if (n < 0 || (n > 0 && !seqs)) return KVM_EINVAL;
+    if (n > kMaxSeqs) return KVM_ERANGE;
+    const int64_t c_kv = int64_t(layout->num_sides) * layout->row_bytes;
+    if (c_kv > INT32_MAX) return KVM_ERANGE;
+    const int64_t dense = int64_t(num_layers) * c_kv;
+    // hit rows: tiles of the fused kernel; miss rows: a merge with no hit part
+    std::vector<kvm::LayerBatch> hit;
+    std::vector<kvm::SeqBatch> keys;   // the same records as an unpack call, for the tile order
+    MergePlan miss(c_kv);
+    uint64_t bits = uint64_t(uintptr_t(pool)) | uint64_t(layout->row_bytes) |
+                    uint64_t(layout->block_stride) | uint64_t(layout->side_stride) |
+                    uint64_t(layout->layer_stride);
+    for (int32_t i = 0; i < n; ++i) {
+        const kvm_layer_seq& s = seqs[i];
+        if (s.t_hit < 0 || s.t_miss < 0 || s.token_stride < 0 || s.miss_stride < 0 ||
+            s.out_stride < 0)
+            return KVM_EINVAL;
+        if (s.t_hit > 0 && (!s.block_table || !s.full)) return KVM_EINVAL;
+        if (s.t_miss > 0 && !s.miss) return KVM_EINVAL;
+        if (s.t_hit + s.t_miss > 0 && !s.out) return KVM_EINVAL;
+        const int64_t ts = s.token_stride ? s.token_stride : dense;
+        if (ts < dense) return KVM_EINVAL;
+        if (s.t_miss > 0) {
+            rc = miss.add(nullptr, 0, 0, s.miss, s.miss_stride, s.t_miss,
+                          static_cast<char*>(s.out) + s.t_hit * s.out_stride, s.out_stride);
+            if (rc != KVM_OK) return rc;
+        }
+        if (s.t_hit == 0) continue;
+        if (hit.empty() || hit.back().n == kvm::kRecsPerLaunch) {
+            hit.emplace_back();
+            keys.emplace_back();
+            std::memset(&hit.back(), 0, sizeof(kvm::LayerBatch));
+            std::memset(&keys.back(), 0, sizeof(kvm::SeqBatch));
+        }
+        kvm::LayerBatch& b = hit.back();
+        kvm::SeqBatch& k = keys.back();
+        const int64_t tiles = (s.t_hit + layout->block_tokens - 1) / layout->block_tokens;
+        if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
+        b.rec[b.n] = {s.block_table, static_cast<const char*>(s.full), s.t_hit, ts,
+                      static_cast<char*>(s.out), s.out_stride};
+        k.rec[k.n] = {s.block_table, static_cast<const char*>(s.full), s.t_hit, ts};
+        b.tile0[b.n + 1] = k.tile0[k.n + 1] = b.tile0[b.n] + tiles;
+        ++b.n;
+        ++k.n;
+        bits |= uint64_t(uintptr_t(s.full)) | uint64_t(ts) | uint64_t(uintptr_t(s.out)) |
+                uint64_t(s.out_stride);
+    }
+    if (hit.empty() && miss.batches.empty()) return KVM_OK;
+    if (!hit.empty() && !pool) return KVM_EINVAL;
+    if (hit.size() > size_t(kOrderSlots)) return KVM_ERANGE;
     const int unit = move_unit(bits);
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    for (const kvm::MergeBatch& b : batches) {
-        hipError_t e = kvm::launch_merge(unit, row_bytes, rows_per_tile, b, st);
-        if (e != hipSuccess) return fail_hip(ctx, e, "k_merge launch");
+    std::vector<OrderSlot*> orders(hit.size(), nullptr);
+    for (size_t i = 0; i < hit.size(); ++i) {
+        if (layout->num_blocks > 16 * hit[i].tile0[hit[i].n] + 65536) continue;
+        rc = unpack_order(ctx, keys[i], layout->num_blocks, st, &orders[i]);
+        if (rc != KVM_OK) return rc;
     }
-    return KVM_OK;
+    const PoolGeom g = geom_of(layout);
+    for (size_t i = 0; i < hit.size(); ++i) {
+        hipError_t e = kvm::launch_unpack_merge(unit, g, static_cast<char*>(pool), layer, hit[i],
+                                                orders[i] ? orders[i]->order : nullptr,
+                                                ctx->d_err, st);
+        if (e == hipSuccess && orders[i]) e = hipEventRecord(orders[i]->last_use, st);
+        if (e != hipSuccess) return fail_hip(ctx, e, "k_unpack_merge launch");
+    }
+    return miss.batches.empty() ? KVM_OK : miss.launch(ctx, st);
 }
 
 int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,

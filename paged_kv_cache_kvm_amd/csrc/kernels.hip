@@ -149,6 +149,8 @@ constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
 constexpr int kUnpackBS = 256, kUnpackUnroll = 8;
 constexpr bool kUnpackWaveMajor = false;
+constexpr int kFusedBS = 256, kFusedUnroll = 8;
+constexpr bool kFusedWaveMajor = false;
 
 // ---------------------------------------------------------------- pack ---
 // full[t][l][s] <- pool[l][s][bt[t / B]][t % B] for the tokens of one block
@@ -218,6 +220,66 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
         sp = src + int64_t(r) * s.token_stride + int64_t(q) * U;
         dp = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
     });
+}
+
+// ---------------------------------------------------- unpack + merge ---
+// The hit rows of one layer, read once and stored twice: into the block-table
+// slots (as k_unpack) and into the request's output rows t0..t0+rows (as the
+// hit part of k_merge). Same tiles, order and element order as k_unpack; the
+// second store of element j goes to out + (t0 + r)*out_stride + q*U.
+template <int U, int BS, int UNR, bool WM>
+__global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restrict__ pool,
+                                                     int32_t layer, const LayerBatch batch,
+                                                     const int32_t* __restrict__ order,
+                                                     FastDiv div_q, FastDiv div_v,
+                                                     unsigned long long* err)
+{
+    typedef typename Unit<U>::T V;
+    const int64_t tile = order ? order[blockIdx.x] : int64_t(blockIdx.x);
+    const int32_t si = find_record(batch.tile0, batch.n, tile);
+    const LayerRec s = batch.rec[si];
+    const int64_t b = tile - batch.tile0[si];
+    const int32_t blk = s.block_table[b];
+    if (bad_block(blk, g.num_blocks)) {
+        if (threadIdx.x == 0) atomicAdd(err, 1ull);
+        return;
+    }
+    const int64_t t0 = b * g.block_tokens;
+    const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
+    const uint32_t total = rows * div_q.d;
+    const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
+    char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
+    char* out = s.out + t0 * s.out_stride;
+    constexpr uint32_t kStep = WM ? 64 : BS;
+    const uint32_t first = WM ? (threadIdx.x >> 6) * (64 * UNR) + (threadIdx.x & 63) : threadIdx.x;
+    const uint32_t limit = WM ? total + BS * UNR : total;
+    for (uint32_t base = first; base < limit; base += BS * UNR) {
+        V v[UNR];
+        char* dp[UNR];
+        char* op[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t j = base + k * kStep;
+            if (j < total) {
+                const uint32_t r = fdiv(j, div_q);
+                const uint32_t q = j - r * div_q.d;
+                const uint32_t side = fdiv(q, div_v);
+                const uint32_t c = q - side * div_v.d;
+                v[k] = ld(reinterpret_cast<const V*>(src + int64_t(r) * s.token_stride +
+                                                     int64_t(q) * U));
+                dp[k] = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+                op[k] = out + int64_t(r) * s.out_stride + int64_t(q) * U;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const uint32_t j = base + k * kStep;
+            if (j < total) {
+                st(reinterpret_cast<V*>(dp[k]), v[k]);
+                st(reinterpret_cast<V*>(op[k]), v[k]);
+            }
+        }
+    }
 }
 
 // --------------------------------------------------------------- merge ---
@@ -510,6 +572,21 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
     hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dq, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_UNPACK)
 #undef KVM_UNPACK
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t layer,
+                               const LayerBatch& b, const int32_t* order,
+                               unsigned long long* err, hipStream_t st)
+{
+    const uint32_t v = uint32_t(g.row_bytes / unit);
+    const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
+    const dim3 grid(uint32_t(b.tile0[b.n]));
+#define KVM_FUSED(U)                                                                        \
+    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, kFusedWaveMajor>), grid,   \
+                       dim3(kFusedBS), 0, st, g, pool, layer, b, order, dq, dv, err)
+    KVM_UNIT_SWITCH(unit, KVM_FUSED)
+#undef KVM_FUSED
     return hipGetLastError();
 }
 

@@ -73,6 +73,23 @@ struct MergeBatch {
     MergeRec rec[kRecsPerLaunch];
 };
 
+// One request of the fused unpack + merge (hit rows only; the miss rows go
+// through k_merge).
+struct LayerRec {
+    const int32_t* block_table;
+    const char* full;
+    int64_t num_tokens;
+    int64_t token_stride;
+    char* out;
+    int64_t out_stride;
+};
+
+struct LayerBatch {
+    int32_t n;
+    int64_t tile0[kRecsPerLaunch + 1];
+    LayerRec rec[kRecsPerLaunch];
+};
+
 struct CopyDesc {
     uint64_t src_off;
     uint64_t dst_off;
@@ -89,6 +106,12 @@ hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t nu
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
                          int32_t layer, const SeqBatch& b, const int32_t* order,
                          unsigned long long* err, hipStream_t st);
+
+// Hit rows of one layer into the pool slots and into the output rows, one
+// read per row; `order` as for launch_unpack (made from the same tables).
+hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t layer,
+                               const LayerBatch& b, const int32_t* order,
+                               unsigned long long* err, hipStream_t st);
 
 // Sort the batch's unpack tiles by destination block id into `order`
 // (b.tile0[b.n] entries). count_scratch holds 2 * (num_blocks + 2) words.

@@ -48,6 +48,14 @@ class kvm_merge_seq(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64)]
 
 
+class kvm_layer_seq(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("full", ctypes.c_void_p),
+                ("t_hit", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("miss", ctypes.c_void_p), ("miss_stride", ctypes.c_int64),
+                ("t_miss", ctypes.c_int64), ("out", ctypes.c_void_p),
+                ("out_stride", ctypes.c_int64)]
+
+
 class kvm_copy_desc(ctypes.Structure):
     _fields_ = [("src_off", ctypes.c_uint64), ("dst_off", ctypes.c_uint64),
                 ("nbytes", ctypes.c_uint64)]
@@ -69,6 +77,8 @@ SIGNATURES = {
     "kvm_unpack_layer": ([_P, ctypes.POINTER(kvm_pool_layout), _P, _I32, _I32,
                           ctypes.POINTER(kvm_seq), _I32, _P], ctypes.c_int),
     "kvm_merge_layer": ([_P, _I64, ctypes.POINTER(kvm_merge_seq), _I32, _P], ctypes.c_int),
+    "kvm_unpack_merge_layer": ([_P, ctypes.POINTER(kvm_pool_layout), _P, _I32, _I32,
+                                ctypes.POINTER(kvm_layer_seq), _I32, _P], ctypes.c_int),
     "kvm_batch_copy": ([_P, _P, _U64, _P, _U64, _P, _I64, _P], ctypes.c_int),
 }
 
@@ -170,6 +180,12 @@ def merge_seq(hit, hit_stride: int, t_hit: int, miss, miss_stride: int, t_miss: 
                          _addr(out), out_stride)
 
 
+def layer_seq(block_table, full, t_hit: int, miss, miss_stride: int, t_miss: int, out,
+              out_stride: int, token_stride: int = 0) -> kvm_layer_seq:
+    return kvm_layer_seq(_addr(block_table), _addr(full), t_hit, token_stride, _addr(miss),
+                         miss_stride, t_miss, _addr(out), out_stride)
+
+
 def _array(cls, items: Sequence):
     items = list(items)
     arr = (cls * max(1, len(items)))(*items)
@@ -196,6 +212,14 @@ def kvm_merge_layer(ctx: int, row_bytes: int, seqs: Iterable[kvm_merge_seq], str
     arr, n = _array(kvm_merge_seq, seqs)
     st = load().kvm_merge_layer(ctx, row_bytes, arr, n, _stream(stream))
     _check("kvm_merge_layer", st, ctx)
+
+
+def kvm_unpack_merge_layer(ctx: int, layout: kvm_pool_layout, pool, num_layers: int, layer: int,
+                           seqs: Iterable[kvm_layer_seq], stream=None) -> None:
+    arr, n = _array(kvm_layer_seq, seqs)
+    st = load().kvm_unpack_merge_layer(ctx, ctypes.byref(layout), _addr(pool), num_layers, layer,
+                                       arr, n, _stream(stream))
+    _check("kvm_unpack_merge_layer", st, ctx)
 
 
 def kvm_batch_copy(ctx: int, dst_base, dst_bytes: int, src_base, src_bytes: int, descs,
@@ -243,6 +267,9 @@ class Context:
 
     def merge_layer(self, row_bytes, seqs, stream=None):
         kvm_merge_layer(self.handle, row_bytes, seqs, stream)
+
+    def unpack_merge_layer(self, layout, pool, num_layers, layer, seqs, stream=None):
+        kvm_unpack_merge_layer(self.handle, layout, pool, num_layers, layer, seqs, stream)
 
     def batch_copy(self, dst_base, dst_bytes, src_base, src_bytes, descs, n_descs, stream=None):
         kvm_batch_copy(self.handle, dst_base, dst_bytes, src_base, src_bytes, descs, n_descs,

@@ -145,3 +145,47 @@ def run_batch_copy(ctx, dev, src_np, dst_np, descs_np, expect_skipped=0, same_bu
     oracle.batch_copy(want, want if same_buffer else src_np, descs_ok)
     assert np.array_equal(down(dst), want), f"batch_copy differs ({label})"
     assert ctx.take_device_errors() == expect_skipped
+
+
+def run_unpack_merge(ctx, dev, L, S, N, B, rb, reqs, kind="dense", ts_pad=0, miss_pad=0,
+                     out_pad=0, offset=0, seed=0):
+    """kvm_unpack_merge_layer against the oracle's unpack_layer followed by
+    merge_layer (its definition), for layers 0 and L-1."""
+    bs, ss, ls, pool_bytes = layout_geometry(kind, L, S, N, B, rb)
+    layout = kv.pool_layout(S, B, rb, bs, ss, ls, N)
+    ref = oracle.pool_struct(S, B, rb, bs, ss, ls, N)
+    C = S * rb
+    ts, ms, os_ = L * C + ts_pad, C + miss_pad, C + out_pad
+    say(f"  fused L={L} S={S} N={N} B={B} rb={rb} reqs={reqs[:3]}{'...' if len(reqs) > 3 else ''}"
+        f" n={len(reqs)} kind={kind} pads=({ts_pad},{miss_pad},{out_pad}) offset={offset}")
+    rng = np.random.default_rng(seed)
+    tables = wl.block_tables(seed, 1, N, [wl.blocks_needed(h + m, B) for h, m in reqs])
+    fb_np = [rng.integers(0, 256, max(h, 1) * ts, dtype=np.uint8) for h, _ in reqs]
+    miss_np = [rng.integers(0, 256, max(m, 1) * ms, dtype=np.uint8) for _, m in reqs]
+    pool_np = rng.integers(0, 256, pool_bytes, dtype=np.uint8)
+    pool = up(pool_np, dev, offset)
+    bts = [up(t, dev) for t in tables]
+    fbs = [up(a, dev, offset) for a in fb_np]
+    misses = [up(a, dev, offset) for a in miss_np]
+    want_pool = pool_np.copy()
+    for layer in sorted({0, L - 1}):
+        want_out = []
+        for i, (h, m) in enumerate(reqs):   # the oracle first: CPU bounds checks
+            oracle.unpack_layer(want_pool, ref, L, layer, tables[i], h, fb_np[i], token_stride=ts)
+            o = np.full(max(h + m, 1) * os_, SENTINEL, np.uint8)
+            oracle.merge_layer(C, fb_np[i][layer * C:] if h else None, ts, h,
+                               miss_np[i] if m else None, ms, m, o, os_)
+            want_out.append(o)
+        outs = [up(np.full(max(h + m, 1) * os_, SENTINEL, np.uint8), dev, offset) for h, m in reqs]
+        seqs = [kv.layer_seq(bts[i] if h else 0, fbs[i].data_ptr() + offset if h else 0, h,
+                             misses[i].data_ptr() + offset if m else 0, ms, m,
+                             outs[i].data_ptr() + offset if h + m else 0, os_,
+                             token_stride=ts if ts_pad else 0)
+                for i, (h, m) in enumerate(reqs)]
+        kv.kvm_unpack_merge_layer(ctx.handle, layout, pool.data_ptr() + offset, L, layer, seqs)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(pool, offset), want_pool), f"pool after layer {layer}"
+        for i in range(len(reqs)):
+            assert np.array_equal(down(outs[i], offset), want_out[i]), \
+                f"complete_layer {layer} request {i}"
+    assert ctx.take_device_errors() == 0

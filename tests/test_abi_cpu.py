@@ -57,6 +57,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(kvmove.kvm_seq) == 32
     assert ctypes.sizeof(kvmove.kvm_merge_seq) == 64
     assert ctypes.sizeof(kvmove.kvm_copy_desc) == 24
+    assert ctypes.sizeof(kvmove.kvm_layer_seq) == 72
 
 
 def test_null_arguments_rejected_without_a_device():

@@ -42,9 +42,11 @@ def need_free(nbytes):
         pytest.fail(f"workload needs {nbytes / 2**30:.1f} GiB, {free / 2**30:.1f} GiB free")
 
 
-def test_llama8b_layer_loop(ctx, gpu):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_llama8b_layer_loop(ctx, gpu, fused):
     """8 x (32768 hit + 512 miss) tokens, 32 layers, B=16, 24576-block pool:
-    unpack_layer + merge_layer for every layer, then pack_full(T_all)."""
+    unpack_layer + merge_layer for every layer (or unpack_merge_layer), then
+    pack_full(T_all)."""
     w = wl.LLAMA8B
     sh = w.shape
     L, S, B, rb, N = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, w.pool_blocks
@@ -53,7 +55,7 @@ def test_llama8b_layer_loop(ctx, gpu):
     t_all = t_hit + t_miss
     slab = S * N * B * rb
     need_free(L * slab + R * (t_hit * L * C + t_miss * L * C + 2 * t_all * L * C) + (1 << 30))
-    say(f"  {w.name} seed={w.seed}")
+    say(f"  {w.name} seed={w.seed} fused={fused}")
     u8 = dict(dtype=torch.uint8, device=gpu)
     pool = torch.empty(L * slab, **u8)
     wl.fill_bf16_normal_(pool, w.seed, 1)
@@ -73,6 +75,12 @@ def test_llama8b_layer_loop(ctx, gpu):
     for l in range(L):
         if l in sample_layers:
             pre[l] = host(pool[l * slab:(l + 1) * slab])
+        if fused:
+            kv.kvm_unpack_merge_layer(ctx.handle, layout, pool, L, l, [
+                kv.layer_seq(bts[r], fbs[r], t_hit, misses[r].data_ptr() + l * C, L * C, t_miss,
+                             complete.data_ptr() + (r * L + l) * t_all * C, C)
+                for r in range(R)])
+            continue
         kv.kvm_unpack_layer(ctx.handle, layout, pool, L, l, unpack_seqs)
         kv.kvm_merge_layer(ctx.handle, C, [
             kv.merge_seq(fbs[r].data_ptr() + l * C, L * C, t_hit, misses[r].data_ptr() + l * C,
@@ -154,10 +162,12 @@ def test_qwen32b_object_restore(ctx, gpu):
     torch.cuda.empty_cache()
 
 
-def test_mla_agentic_layer_loop(ctx, gpu):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_mla_agentic_layer_loop(ctx, gpu, fused):
     """64 requests, T_hit ~ U{16384..65536}, T_miss ~ U{128..1024}, 61 layers of
     one 576-element latent, B=64, one-layer slot pool: per layer unpack of the
-    hit slice, then merge with that layer's miss rows into a 2-deep ring."""
+    hit slice, then merge with that layer's miss rows into a 2-deep ring (or
+    both in one unpack_merge_layer call)."""
     w = wl.mla_agentic()
     sh = w.shape
     L, S, B, rb, C = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, sh.c_kv_bytes
@@ -170,7 +180,7 @@ def test_mla_agentic_layer_loop(ctx, gpu):
     ring = [sum(t * C for t in w.t_all)] * 2
     need_free(sum(fb_bytes) + L * sum(miss_bytes) + slot_bytes + sum(ring) + (2 << 30))
     say(f"  {w.name}: sum T_hit={sum(w.t_hit)}, Full Blocks {sum(fb_bytes) / 2**30:.1f} GiB, "
-        f"slot pool {N} blocks")
+        f"slot pool {N} blocks, fused={fused}")
     u8 = dict(dtype=torch.uint8, device=gpu)
     tables = wl.block_tables(w.seed, 2, N, per_req)
     bts = [torch.from_numpy(t).to(gpu) for t in tables]
@@ -193,10 +203,15 @@ def test_mla_agentic_layer_loop(ctx, gpu):
         pre = host(slot) if l in sample_layers else None
         mbase = misses.data_ptr() + l * int(moff[-1])
         out = rings[l % 2]
-        kv.kvm_unpack_layer(ctx.handle, layout, slot, L, l, seqs)
-        kv.kvm_merge_layer(ctx.handle, C, [
-            kv.merge_seq(fbs[r].data_ptr() + l * C, L * C, w.t_hit[r], mbase + int(moff[r]), C,
-                         w.t_miss[r], out.data_ptr() + int(roff[r]), C) for r in range(R)])
+        if fused:
+            kv.kvm_unpack_merge_layer(ctx.handle, layout, slot, L, l, [
+                kv.layer_seq(bts[r], fbs[r], w.t_hit[r], mbase + int(moff[r]), C, w.t_miss[r],
+                             out.data_ptr() + int(roff[r]), C) for r in range(R)])
+        else:
+            kv.kvm_unpack_layer(ctx.handle, layout, slot, L, l, seqs)
+            kv.kvm_merge_layer(ctx.handle, C, [
+                kv.merge_seq(fbs[r].data_ptr() + l * C, L * C, w.t_hit[r], mbase + int(moff[r]),
+                             C, w.t_miss[r], out.data_ptr() + int(roff[r]), C) for r in range(R)])
         if pre is None:
             continue
         torch.cuda.synchronize()

@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import SENTINEL, down, run_batch_copy, run_merge, run_pack_unpack, say, up
+from gpu_util import (SENTINEL, down, run_batch_copy, run_merge, run_pack_unpack,
+                      run_unpack_merge, say, up)
 from paged_kv_cache_kvm_amd import kvmove as kv
 from paged_kv_cache_kvm_amd import workloads as wl
 
@@ -279,3 +280,21 @@ def test_unpack_order_cache_eviction(ctx, gpu):
         kv.kvm_unpack_layer(ctx.handle, layout, pool, L, l, [kv.seq(bt, fb, T)])
     torch.cuda.synchronize()
     assert np.array_equal(down(pool), want)
+
+
+FUSED_CASES = [
+    # (L, S, N, B, rb, reqs, kind, ts_pad, miss_pad, out_pad, offset)
+    (4, 2, 64, 16, 256, [(240, 16)], "dense", 0, 0, 0, 0),
+    (3, 2, 200, 16, 512, [(300, 20), (0, 9), (13, 0), (0, 0), (64, 64)], "dense", 0, 0, 0, 0),
+    (3, 1, 300, 64, 1152, [(700, 77), (65, 3)], "slot", 0, 0, 128, 0),
+    (2, 2, 700, 3, 48, [(5, 2), (1, 1)] * 70, "block_major", 0, 0, 0, 0),   # 140 requests
+    (2, 2, 60, 4, 12, [(23, 5), (9, 0)], "dense", 4, 4, 4, 4),               # 4-byte moves
+    (2, 2, 60, 4, 5, [(23, 5), (9, 2)], "dense", 3, 1, 5, 1),                # byte moves
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[f"fused{i}" for i in range(len(FUSED_CASES))])
+def test_unpack_merge(ctx, gpu, case):
+    L, S, N, B, rb, reqs, kind, tp, mp, op, off = case
+    run_unpack_merge(ctx, gpu, L, S, N, B, rb, reqs, kind=kind, ts_pad=tp, miss_pad=mp,
+                     out_pad=op, offset=off, seed=hash(str(case)) & 0xFFFF)
