@@ -256,10 +256,10 @@ PROFILE = os.path.join(ROOT, "profiles", "llama8b_layer_loop_hbm_traffic.md")
 KERNEL_SOURCES = ("paged_kv_cache_kvm_amd/csrc/kernels.hip", "paged_kv_cache_kvm_amd/csrc/kvm_internal.h")
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when that summary was taken on other kernel
-    sources than the ones built now."""
+def measured_traffic(op):
+    """HBM bytes per launch of `op`'s kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when that summary was taken on
+    other kernel sources than the ones built now."""
     import hashlib
     try:
         line = next(l for l in open(PROFILE) if l.startswith("traffic-json: "))
@@ -271,7 +271,7 @@ def measured_traffic(kernel):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if rec.get("kernel_source_sha256") != h.hexdigest():
         return None
-    return rec["bytes_per_launch"].get(kernel)
+    return rec["bytes_per_launch"].get(op)
 
 
 def main():
@@ -351,7 +351,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "op": dom,
                      "achieved": ops[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ops[dom]["GBps"] / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(kernel),
+                     "traffic": measured_traffic(dom),
                      "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"]},
         "fused_layer_loop": fused,
         "copy_ceiling_GBps": round(ceiling, 1),
