@@ -10,11 +10,13 @@ request. All inputs are resident in HBM before timing.
 value = algorithmic bytes (read + write) of one step / step time, whole job.
 Also reported: each op's average launch time from HIP events on the launch
 stream, the roofline of the dominant kernel, the same step with unpack and
-merge fused per layer (kvm_unpack_merge_layer), a device copy ceiling, the
+merge fused per layer (kvm_unpack_merge_layer), the host tier (a pinned host
+Full Block / complete_layer over PCIe), a device copy ceiling, the
 small-object batched copy (200000 objects of 256*U{16..512} bytes) and the
 oracle timed on the host cores on one request of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-batch-copy]
+                      [--no-host]
 """
 from __future__ import annotations
 
@@ -42,6 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-batch-copy", action="store_true", help="skip the batched-copy section")
+    ap.add_argument("--no-host", action="store_true", help="skip the pinned-host-buffer section")
     return ap.parse_args()
 
 
@@ -160,6 +163,59 @@ def fused_section(torch, kv, ctx, s, steps, warmup, step_bytes, ms_separate):
             "unpack_merge_layer": {"bytes_per_launch": s["bytes_fused"],
                                    "ms_per_launch": round(per, 4), "GBps": round(gbs, 1),
                                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}}
+
+
+def host_tier_section(torch, kv, ctx, s, reps=3):
+    """The pages' host-DRAM prompt buffers: request 0's Full Block in pinned host
+    memory. Per layer: unpack_layer reads its hit slice over PCIe into the HBM
+    pool (Prefill side); merge_layer writes complete_layer into a pinned host
+    buffer (Decode side, hit rows from HBM). Rates are PCIe bytes per second,
+    next to torch's pinned host<->device copy rates."""
+    L, C = s["L"], s["C"]
+    bts, fbs, misses, _, _ = s["keep"]
+    t_hit, t_miss = 32768, 512
+    t_all = t_hit + t_miss
+    host_fb = torch.empty(fbs[0].numel(), dtype=torch.uint8, pin_memory=True)
+    host_fb.copy_(fbs[0])
+    host_out = torch.empty(t_all * C, dtype=torch.uint8, pin_memory=True)
+    dev_buf = torch.empty(1 << 30, dtype=torch.uint8, device=fbs[0].device)
+    host_buf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    seqs = [kv.seq(bts[0], host_fb, t_hit)]
+    ev = Events(torch)
+
+    def unpack_loop():
+        for l in range(L):
+            kv.kvm_unpack_layer(ctx.handle, s["layout"], s["pool"], L, l, seqs)
+
+    def merge_loop():
+        for l in range(L):
+            kv.kvm_merge_layer(ctx.handle, C, [kv.merge_seq(
+                fbs[0].data_ptr() + l * C, L * C, t_hit, misses[0].data_ptr() + l * C, L * C,
+                t_miss, host_out, C)])
+
+    unpack_loop()
+    merge_loop()
+    for _ in range(reps):
+        ev.around("h2d_unpack", unpack_loop)
+        ev.around("d2h_merge", merge_loop)
+        ev.around("h2d_copy", lambda: dev_buf.copy_(host_buf, non_blocking=True))
+        ev.around("d2h_copy", lambda: host_buf.copy_(dev_buf, non_blocking=True))
+    torch.cuda.synchronize()
+    up_gbs = L * t_hit * C / (ev.mean_ms("h2d_unpack") * 1e6)
+    mg_gbs = L * t_all * C / (ev.mean_ms("d2h_merge") * 1e6)
+    h2d = (1 << 30) / (ev.mean_ms("h2d_copy") * 1e6)
+    d2h = (1 << 30) / (ev.mean_ms("d2h_copy") * 1e6)
+    del host_fb, host_out, dev_buf, host_buf
+    return {"workload": "request 0 of the layer loop, Full Block / complete_layer in pinned host memory",
+            "unpack_layer_from_host": {"pcie_bytes_per_launch": t_hit * C,
+                                       "ms_per_launch": round(ev.mean_ms("h2d_unpack") / L, 3),
+                                       "pcie_GBps": round(up_gbs, 1),
+                                       "frac_of_h2d_copy": round(up_gbs / h2d, 3)},
+            "merge_layer_into_host": {"pcie_bytes_per_launch": t_all * C,
+                                      "ms_per_launch": round(ev.mean_ms("d2h_merge") / L, 3),
+                                      "pcie_GBps": round(mg_gbs, 1),
+                                      "frac_of_d2h_copy": round(mg_gbs / d2h, 3)},
+            "torch_pinned_copy_GBps": {"h2d": round(h2d, 1), "d2h": round(d2h, 1)}}
 
 
 def copy_ceiling(torch, dev, nbytes=2 << 30, reps=10):
@@ -325,6 +381,7 @@ def main():
                      "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
     dom = max(ops, key=lambda k: ops[k]["ms_per_launch"] * ops[k]["launches_per_step"])
     fused = fused_section(torch, kv, ctx, s, args.steps, args.warmup, step_bytes, ms_step)
+    host = None if args.no_host else host_tier_section(torch, kv, ctx, s)
     assert ctx.take_device_errors() == 0
     workload = s["w"].name
     del s
@@ -354,6 +411,7 @@ def main():
                      "traffic": measured_traffic(dom),
                      "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"]},
         "fused_layer_loop": fused,
+        "host_tier": host,
         "copy_ceiling_GBps": round(ceiling, 1),
         "batch_copy": bc,
         "cpu_baseline": cpu,

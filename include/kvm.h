@@ -30,7 +30,10 @@
  *     "back to the real objects": an enqueued copy is not a finished copy.
  *
  * Conventions for every call
- *   - Device pointers are HIP device addresses on the context's device. Host
+ *   - Device pointers are HIP device addresses on the context's device. A Full
+ *     Block, miss rows or complete_layer may also live in pinned host memory
+ *     (hipHostMalloc): the kernels then read or write it over PCIe through its
+ *     device-visible address (DualPath's host-DRAM prompt buffers). Host
  *     arrays (kvm_seq, kvm_merge_seq) are read during the call and may be
  *     reused as soon as it returns: their contents travel to the kernels as
  *     kernel arguments, up to 128 records per launch.
