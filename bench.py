@@ -11,12 +11,13 @@ value = algorithmic bytes (read + write) of one step / step time, whole job.
 Also reported: each op's average launch time from HIP events on the launch
 stream, the roofline of the dominant kernel, the same step with unpack and
 merge fused per layer (kvm_unpack_merge_layer), the host tier (a pinned host
-Full Block / complete_layer over PCIe), a device copy ceiling, the
+Full Block / complete_layer over PCIe), the layerwise overlap of the moves
+with a stand-in compute stream under workgroup budgets, a device copy ceiling, the
 small-object batched copy (200000 objects of 256*U{16..512} bytes) and the
 oracle timed on the host cores on one request of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-batch-copy]
-                      [--no-host]
+                      [--no-host] [--no-pipeline]
 """
 from __future__ import annotations
 
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-batch-copy", action="store_true", help="skip the batched-copy section")
     ap.add_argument("--no-host", action="store_true", help="skip the pinned-host-buffer section")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the layerwise overlap section (workgroup-bounded moves)")
     return ap.parse_args()
 
 
@@ -218,6 +221,105 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
             "torch_pinned_copy_GBps": {"h2d": round(h2d, 1), "d2h": round(d2h, 1)}}
 
 
+def pipeline_section(torch, kv, ctx, s, reps=3, d_model=4096, d_ff=14336):
+    """Layerwise overlap of the KV moves with compute, the moves bounded to a
+    workgroup budget (kvm_ctx_set_max_workgroups).
+
+    (1) The fused layer loop (L x unpack_merge_layer) alone at budgets k: how
+    many workgroups the moves need to reach HBM speed. (2) A stand-in for each
+    layer's compute, the MLP GEMMs of the step's miss tokens (R * T_miss rows,
+    bf16, d_model -> 2*d_ff -> d_model, random weights), on a second stream,
+    while the moves run up to one layer ahead on the first; layer l's compute waits for layer
+    l's moves and layer l's moves wait for layer l-2's compute (two layer
+    buffers). Timed against the same work run back to back on one stream."""
+    L = s["L"]
+    layers = s["fused_by_layer"]
+    rows = sum(t for t in s["w"].t_miss)
+    st_kv, st_cmp = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(rows, d_model, device="cuda", dtype=torch.bfloat16, generator=g)
+    w_up = torch.randn(d_model, 2 * d_ff, device="cuda", dtype=torch.bfloat16, generator=g)
+    w_down = torch.randn(d_ff, d_model, device="cuda", dtype=torch.bfloat16, generator=g)
+    h = torch.empty(rows, 2 * d_ff, device="cuda", dtype=torch.bfloat16)
+    y = torch.empty(rows, d_model, device="cuda", dtype=torch.bfloat16)
+    flops_layer = 2 * rows * d_model * 2 * d_ff + 2 * rows * d_ff * d_model
+
+    def moves(l, st=None):
+        kv.kvm_unpack_merge_layer(ctx.handle, s["layout"], s["pool"], L, l, layers[l], stream=st)
+
+    def compute():
+        torch.mm(x, w_up, out=h)
+        torch.mm(h[:, :d_ff], w_down, out=y)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) * 1e3
+            best = dt if best is None else min(best, dt)
+        return best
+
+    def serial():
+        for l in range(L):
+            moves(l)
+            compute()
+
+    def overlapped():
+        # two layer buffers: layer l's moves wait until layer l-2's compute is
+        # done, layer l's compute waits for its moves
+        ready = [torch.cuda.Event() for _ in range(L)]
+        done = [torch.cuda.Event() for _ in range(L)]
+        st_kv.wait_stream(torch.cuda.current_stream())
+        st_cmp.wait_stream(torch.cuda.current_stream())
+        for l in range(L):
+            if l >= 2:
+                st_kv.wait_event(done[l - 2])
+            moves(l, st_kv)
+            ready[l].record(st_kv)
+            with torch.cuda.stream(st_cmp):
+                st_cmp.wait_event(ready[l])
+                compute()
+                done[l].record(st_cmp)
+        torch.cuda.current_stream().wait_stream(st_cmp)
+        torch.cuda.current_stream().wait_stream(st_kv)
+
+    def compute_all():
+        for _ in range(L):
+            compute()
+
+    try:
+        curve = {}
+        for k in (16, 32, 64, 128, 256, 512, 1024, 0):
+            ctx.set_max_workgroups(k)
+            ms = timed(lambda: [moves(l) for l in range(L)])
+            curve[str(k) if k else "unbounded"] = round(L * s["bytes_fused"] / (ms * 1e6), 1)
+        ctx.set_max_workgroups(0)
+        t_moves = timed(lambda: [moves(l) for l in range(L)])
+        t_comp = timed(compute_all)
+        t_serial = timed(serial)
+        over = {}
+        for k in (64, 128, 256, 512, 0):
+            ctx.set_max_workgroups(k)
+            t = timed(overlapped)
+            over[str(k) if k else "unbounded"] = {
+                "ms": round(t, 3),
+                "fraction_of_shorter_hidden": round((t_serial - t) / min(t_moves, t_comp), 3)}
+    finally:
+        ctx.set_max_workgroups(0)
+        torch.cuda.synchronize()
+    return {"moves_GBps_by_workgroup_budget": curve,
+            "stand_in_compute": f"per layer: bf16 GEMMs {rows}x{d_model}x{2 * d_ff} and "
+                                f"{rows}x{d_ff}x{d_model} (MLP of the miss tokens)",
+            "compute_TFLOPs": round(L * flops_layer / (t_comp * 1e9), 1),
+            "ms_moves_alone": round(t_moves, 3), "ms_compute_alone": round(t_comp, 3),
+            "ms_back_to_back": round(t_serial, 3),
+            "ms_overlapped_by_workgroup_budget": over}
+
+
 def copy_ceiling(torch, dev, nbytes=2 << 30, reps=10):
     """Device-to-device copy of nbytes through torch (hipMemcpy), read+write GB/s."""
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -382,6 +484,7 @@ def main():
     dom = max(ops, key=lambda k: ops[k]["ms_per_launch"] * ops[k]["launches_per_step"])
     fused = fused_section(torch, kv, ctx, s, args.steps, args.warmup, step_bytes, ms_step)
     host = None if args.no_host else host_tier_section(torch, kv, ctx, s)
+    pipe = None if args.no_pipeline else pipeline_section(torch, kv, ctx, s)
     assert ctx.take_device_errors() == 0
     workload = s["w"].name
     del s
@@ -412,6 +515,7 @@ def main():
                      "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"]},
         "fused_layer_loop": fused,
         "host_tier": host,
+        "pipeline": pipe,
         "copy_ceiling_GBps": round(ceiling, 1),
         "batch_copy": bc,
         "cpu_baseline": cpu,

@@ -172,6 +172,21 @@ void kvm_destroy(kvm_ctx* ctx);
  * KVM_EHIP. */
 int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
 
+/* Workgroup budget: every later pack, unpack, merge, fused and batched-copy
+ * launch through this context uses a grid of at most max_workgroups
+ * workgroups, each of which loops over the tiles (or byte shares) that a
+ * full-size grid would spread over more workgroups. The moves then occupy a
+ * bounded share of the CUs, so that a layer's moves can run beside the
+ * previous layer's compute on another stream (DualPath KV Loading, layerwise
+ * Prefill; Tutti reading notes, design 2: I/O kernels kept to a few SMs
+ * beside compute). The bytes written are the same for every budget.
+ * 0 (the default) means one workgroup per tile. The destination-order sort
+ * that unpack runs once per new set of block tables is not bounded (it
+ * touches 8 bytes per tile). Applies to calls enqueued
+ * after it returns; calls already enqueued keep their grids. Errors:
+ * KVM_EINVAL (null ctx, max_workgroups < 0). */
+int kvm_ctx_set_max_workgroups(kvm_ctx* ctx, int32_t max_workgroups);
+
 /* Text of the last HIP failure seen by this context ("" if none). */
 const char* kvm_ctx_last_error(const kvm_ctx* ctx);
 

@@ -50,6 +50,7 @@ struct OrderSlot {
 struct kvm_ctx {
     int device = 0;
     int num_cus = 0;
+    int32_t max_wgs = 0;           // workgroup budget of every move launch; 0 = none
     unsigned long long* d_err = nullptr;
     uint64_t* d_groups = nullptr;  // group sums, then group bases
     int64_t group_cap = 0;         // groups the scratch holds
@@ -344,7 +345,7 @@ struct MergePlan {
     {
         const int unit = move_unit(bits);
         for (const kvm::MergeBatch& b : batches) {
-            hipError_t e = kvm::launch_merge(unit, row_bytes, rows_per_tile, b, st);
+            hipError_t e = kvm::launch_merge(unit, row_bytes, rows_per_tile, b, ctx->max_wgs, st);
             if (e != hipSuccess) return fail_hip(ctx, e, "k_merge launch");
         }
         return KVM_OK;
@@ -433,6 +434,13 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs)
     return grow_groups(ctx, (max_descs + kvm::kDescGroup - 1) / kvm::kDescGroup);
 }
 
+int kvm_ctx_set_max_workgroups(kvm_ctx* ctx, int32_t max_workgroups)
+{
+    if (!ctx || max_workgroups < 0) return KVM_EINVAL;
+    ctx->max_wgs = max_workgroups;
+    return KVM_OK;
+}
+
 const char* kvm_ctx_last_error(const kvm_ctx* ctx) { return ctx ? ctx->last_error.c_str() : ""; }
 
 int kvm_take_device_errors(kvm_ctx* ctx, int64_t* count)
@@ -494,10 +502,11 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
         hipError_t e;
         if (pack) {
             e = kvm::launch_pack(unit, g, static_cast<const char*>(pool), num_layers, b, ctx->d_err,
-                                 st);
+                                 ctx->max_wgs, st);
         } else {
             e = kvm::launch_unpack(unit, g, static_cast<char*>(const_cast<void*>(pool)), num_layers,
-                                   layer, b, orders[i] ? orders[i]->order : nullptr, ctx->d_err, st);
+                                   layer, b, orders[i] ? orders[i]->order : nullptr, ctx->d_err,
+                                   ctx->max_wgs, st);
             if (e == hipSuccess && orders[i]) e = hipEventRecord(orders[i]->last_use, st);
         }
         if (e != hipSuccess) return fail_hip(ctx, e, pack ? "k_pack launch" : "k_unpack launch");
@@ -609,7 +618,7 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
     for (size_t i = 0; i < hit.size(); ++i) {
         hipError_t e = kvm::launch_unpack_merge(unit, g, static_cast<char*>(pool), layer, hit[i],
                                                 orders[i] ? orders[i]->order : nullptr,
-                                                ctx->d_err, st);
+                                                ctx->d_err, ctx->max_wgs, st);
         if (e == hipSuccess && orders[i]) e = hipEventRecord(orders[i]->last_use, st);
         if (e != hipSuccess) return fail_hip(ctx, e, "k_unpack_merge launch");
     }
@@ -628,9 +637,10 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     const int64_t groups = (n_descs + kvm::kDescGroup - 1) / kvm::kDescGroup;
     int rc = grow_groups(ctx, groups);
     if (rc != KVM_OK) return rc;
-    // Enough wavefronts to cover every CU several times over; each takes an
-    // equal share of the bytes.
-    const int32_t copy_blocks = ctx->num_cus * 8;
+    // Enough wavefronts to cover every CU several times over, or the
+    // workgroup budget if smaller; each takes an equal share of the bytes.
+    const int32_t copy_blocks =
+        ctx->max_wgs > 0 ? std::min(ctx->max_wgs, ctx->num_cus * 8) : ctx->num_cus * 8;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (ctx->copy_pending && ctx->copy_stream != st) {

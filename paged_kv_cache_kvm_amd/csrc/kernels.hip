@@ -7,6 +7,10 @@
 //
 //   k_pack / k_unpack   one workgroup per tile. A pack tile is (sequence,
 //                       block, layer); an unpack tile is (sequence, block).
+//                       With a workgroup budget below the tile count, the
+//                       grid is the budget and workgroup i takes tiles i,
+//                       i + grid, i + 2*grid, ... (this bounds how many CUs
+//                       the moves occupy while other work shares the GPU).
 //                       A tile's rows (B tokens x sides) are flattened into
 //                       one index space of `unit`-byte elements so that a
 //                       1152-byte MLA row or a 256-byte tiny row keeps all 256
@@ -162,29 +166,32 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
                                              FastDiv div_q, FastDiv div_v,
                                              unsigned long long* err)
 {
-    const int64_t tile = blockIdx.x;
-    const int32_t si = find_record(batch.tile0, batch.n, tile);
-    const SeqRec s = batch.rec[si];
-    const int64_t rem = tile - batch.tile0[si];
-    const int64_t b = rem / num_layers;
-    const int32_t l = int32_t(rem - b * num_layers);
-    const int32_t blk = s.block_table[b];
-    if (bad_block(blk, g.num_blocks)) {
-        if (threadIdx.x == 0) atomicAdd(err, 1ull);
-        return;
+    const int64_t ntiles = batch.tile0[batch.n];
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int32_t si = find_record(batch.tile0, batch.n, tile);
+        const SeqRec s = batch.rec[si];
+        const int64_t rem = tile - batch.tile0[si];
+        const int64_t b = rem / num_layers;
+        const int32_t l = int32_t(rem - b * num_layers);
+        const int32_t blk = s.block_table[b];
+        if (bad_block(blk, g.num_blocks)) {
+            if (threadIdx.x == 0) atomicAdd(err, 1ull);
+            continue;
+        }
+        const int64_t t0 = b * g.block_tokens;
+        const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
+        const char* src = pool + l * g.layer_stride + blk * g.block_stride;
+        char* dst = const_cast<char*>(s.full) + t0 * s.token_stride +
+                    int64_t(l) * g.sides * g.row_bytes;
+        copy_elements<U, BS, UNR, WM>(rows * div_q.d, [&](uint32_t j, const char*& sp, char*& dp) {
+            const uint32_t r = fdiv(j, div_q);
+            const uint32_t q = j - r * div_q.d;
+            const uint32_t side = fdiv(q, div_v);
+            const uint32_t c = q - side * div_v.d;
+            sp = src + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+            dp = dst + int64_t(r) * s.token_stride + int64_t(q) * U;
+        });
     }
-    const int64_t t0 = b * g.block_tokens;
-    const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-    const char* src = pool + l * g.layer_stride + blk * g.block_stride;
-    char* dst = const_cast<char*>(s.full) + t0 * s.token_stride + int64_t(l) * g.sides * g.row_bytes;
-    copy_elements<U, BS, UNR, WM>(rows * div_q.d, [&](uint32_t j, const char*& sp, char*& dp) {
-        const uint32_t r = fdiv(j, div_q);
-        const uint32_t q = j - r * div_q.d;
-        const uint32_t side = fdiv(q, div_v);
-        const uint32_t c = q - side * div_v.d;
-        sp = src + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
-        dp = dst + int64_t(r) * s.token_stride + int64_t(q) * U;
-    });
 }
 
 // -------------------------------------------------------------- unpack ---
@@ -199,27 +206,30 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
                                                FastDiv div_q, FastDiv div_v,
                                                unsigned long long* err)
 {
-    const int64_t tile = order ? order[blockIdx.x] : int64_t(blockIdx.x);
-    const int32_t si = find_record(batch.tile0, batch.n, tile);
-    const SeqRec s = batch.rec[si];
-    const int64_t b = tile - batch.tile0[si];
-    const int32_t blk = s.block_table[b];
-    if (bad_block(blk, g.num_blocks)) {
-        if (threadIdx.x == 0) atomicAdd(err, 1ull);
-        return;
+    const int64_t ntiles = batch.tile0[batch.n];
+    for (int64_t i = blockIdx.x; i < ntiles; i += gridDim.x) {
+        const int64_t tile = order ? order[i] : i;
+        const int32_t si = find_record(batch.tile0, batch.n, tile);
+        const SeqRec s = batch.rec[si];
+        const int64_t b = tile - batch.tile0[si];
+        const int32_t blk = s.block_table[b];
+        if (bad_block(blk, g.num_blocks)) {
+            if (threadIdx.x == 0) atomicAdd(err, 1ull);
+            continue;
+        }
+        const int64_t t0 = b * g.block_tokens;
+        const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
+        const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
+        char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
+        copy_elements<U, BS, UNR, WM>(rows * div_q.d, [&](uint32_t j, const char*& sp, char*& dp) {
+            const uint32_t r = fdiv(j, div_q);
+            const uint32_t q = j - r * div_q.d;
+            const uint32_t side = fdiv(q, div_v);
+            const uint32_t c = q - side * div_v.d;
+            sp = src + int64_t(r) * s.token_stride + int64_t(q) * U;
+            dp = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+        });
     }
-    const int64_t t0 = b * g.block_tokens;
-    const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-    const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
-    char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
-    copy_elements<U, BS, UNR, WM>(rows * div_q.d, [&](uint32_t j, const char*& sp, char*& dp) {
-        const uint32_t r = fdiv(j, div_q);
-        const uint32_t q = j - r * div_q.d;
-        const uint32_t side = fdiv(q, div_v);
-        const uint32_t c = q - side * div_v.d;
-        sp = src + int64_t(r) * s.token_stride + int64_t(q) * U;
-        dp = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
-    });
 }
 
 // ---------------------------------------------------- unpack + merge ---
@@ -235,48 +245,51 @@ __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restric
                                                      unsigned long long* err)
 {
     typedef typename Unit<U>::T V;
-    const int64_t tile = order ? order[blockIdx.x] : int64_t(blockIdx.x);
-    const int32_t si = find_record(batch.tile0, batch.n, tile);
-    const LayerRec s = batch.rec[si];
-    const int64_t b = tile - batch.tile0[si];
-    const int32_t blk = s.block_table[b];
-    if (bad_block(blk, g.num_blocks)) {
-        if (threadIdx.x == 0) atomicAdd(err, 1ull);
-        return;
-    }
-    const int64_t t0 = b * g.block_tokens;
-    const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-    const uint32_t total = rows * div_q.d;
-    const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
-    char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
-    char* out = s.out + t0 * s.out_stride;
-    constexpr uint32_t kStep = WM ? 64 : BS;
-    const uint32_t first = WM ? (threadIdx.x >> 6) * (64 * UNR) + (threadIdx.x & 63) : threadIdx.x;
-    const uint32_t limit = WM ? total + BS * UNR : total;
-    for (uint32_t base = first; base < limit; base += BS * UNR) {
-        V v[UNR];
-        char* dp[UNR];
-        char* op[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const uint32_t j = base + k * kStep;
-            if (j < total) {
-                const uint32_t r = fdiv(j, div_q);
-                const uint32_t q = j - r * div_q.d;
-                const uint32_t side = fdiv(q, div_v);
-                const uint32_t c = q - side * div_v.d;
-                v[k] = ld(reinterpret_cast<const V*>(src + int64_t(r) * s.token_stride +
-                                                     int64_t(q) * U));
-                dp[k] = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
-                op[k] = out + int64_t(r) * s.out_stride + int64_t(q) * U;
-            }
+    const int64_t ntiles = batch.tile0[batch.n];
+    for (int64_t i = blockIdx.x; i < ntiles; i += gridDim.x) {
+        const int64_t tile = order ? order[i] : i;
+        const int32_t si = find_record(batch.tile0, batch.n, tile);
+        const LayerRec s = batch.rec[si];
+        const int64_t b = tile - batch.tile0[si];
+        const int32_t blk = s.block_table[b];
+        if (bad_block(blk, g.num_blocks)) {
+            if (threadIdx.x == 0) atomicAdd(err, 1ull);
+            continue;
         }
+        const int64_t t0 = b * g.block_tokens;
+        const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
+        const uint32_t total = rows * div_q.d;
+        const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
+        char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
+        char* out = s.out + t0 * s.out_stride;
+        constexpr uint32_t kStep = WM ? 64 : BS;
+        const uint32_t first = WM ? (threadIdx.x >> 6) * (64 * UNR) + (threadIdx.x & 63) : threadIdx.x;
+        const uint32_t limit = WM ? total + BS * UNR : total;
+        for (uint32_t base = first; base < limit; base += BS * UNR) {
+            V v[UNR];
+            char* dp[UNR];
+            char* op[UNR];
 #pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const uint32_t j = base + k * kStep;
-            if (j < total) {
-                st(reinterpret_cast<V*>(dp[k]), v[k]);
-                st(reinterpret_cast<V*>(op[k]), v[k]);
+            for (int k = 0; k < UNR; ++k) {
+                const uint32_t j = base + k * kStep;
+                if (j < total) {
+                    const uint32_t r = fdiv(j, div_q);
+                    const uint32_t q = j - r * div_q.d;
+                    const uint32_t side = fdiv(q, div_v);
+                    const uint32_t c = q - side * div_v.d;
+                    v[k] = ld(reinterpret_cast<const V*>(src + int64_t(r) * s.token_stride +
+                                                         int64_t(q) * U));
+                    dp[k] = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+                    op[k] = out + int64_t(r) * s.out_stride + int64_t(q) * U;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                const uint32_t j = base + k * kStep;
+                if (j < total) {
+                    st(reinterpret_cast<V*>(dp[k]), v[k]);
+                    st(reinterpret_cast<V*>(op[k]), v[k]);
+                }
             }
         }
     }
@@ -289,20 +302,22 @@ template <int U, int BS, int UNR, bool WM>
 __global__ __launch_bounds__(BS) void k_merge(int32_t rows_per_tile, const MergeBatch batch,
                                               FastDiv div_v)
 {
-    const int64_t tile = blockIdx.x;
-    const int32_t si = find_record(batch.tile0, batch.n, tile);
-    const MergeRec m = batch.rec[si];
-    const int64_t row0 = (tile - batch.tile0[si]) * rows_per_tile;
-    const int64_t t_all = m.t_hit + m.t_miss;
-    const uint32_t rows = uint32_t(min(int64_t(rows_per_tile), t_all - row0));
-    copy_elements<U, BS, UNR, WM>(rows * div_v.d, [&](uint32_t j, const char*& sp, char*& dp) {
-        const uint32_t r = fdiv(j, div_v);
-        const uint32_t c = j - r * div_v.d;
-        const int64_t row = row0 + r;
-        sp = (row < m.t_hit ? m.hit + row * m.hit_stride
-                            : m.miss + (row - m.t_hit) * m.miss_stride) + int64_t(c) * U;
-        dp = m.out + row * m.out_stride + int64_t(c) * U;
-    });
+    const int64_t ntiles = batch.tile0[batch.n];
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int32_t si = find_record(batch.tile0, batch.n, tile);
+        const MergeRec m = batch.rec[si];
+        const int64_t row0 = (tile - batch.tile0[si]) * rows_per_tile;
+        const int64_t t_all = m.t_hit + m.t_miss;
+        const uint32_t rows = uint32_t(min(int64_t(rows_per_tile), t_all - row0));
+        copy_elements<U, BS, UNR, WM>(rows * div_v.d, [&](uint32_t j, const char*& sp, char*& dp) {
+            const uint32_t r = fdiv(j, div_v);
+            const uint32_t c = j - r * div_v.d;
+            const int64_t row = row0 + r;
+            sp = (row < m.t_hit ? m.hit + row * m.hit_stride
+                                : m.miss + (row - m.t_hit) * m.miss_stride) + int64_t(c) * U;
+            dp = m.out + row * m.out_stride + int64_t(c) * U;
+        });
+    }
 }
 
 // -------------------------------------------------- unpack tile order ---
@@ -530,12 +545,19 @@ __global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__
     default: CALL(1); break;                          \
     }
 
+// Grid of a tile kernel: one workgroup per tile, or the budget if smaller.
+static dim3 tile_grid(int64_t ntiles, int32_t max_wgs)
+{
+    return dim3(uint32_t(max_wgs > 0 ? std::min<int64_t>(ntiles, max_wgs) : ntiles));
+}
+
 hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
-                       const SeqBatch& b, unsigned long long* err, hipStream_t st)
+                       const SeqBatch& b, unsigned long long* err, int32_t max_wgs,
+                       hipStream_t st)
 {
     const uint32_t v = uint32_t(g.row_bytes / unit);
     const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
-    const dim3 grid(uint32_t(b.tile0[b.n]));
+    const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
 #define KVM_PACK(U)                                                                         \
     hipLaunchKernelGGL((k_pack<U, kPackBS, kPackUnroll, kPackWaveMajor>), grid, dim3(kPackBS), 0, st, g, pool, num_layers, b, dq, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_PACK)
@@ -562,12 +584,12 @@ hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* 
 
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
                          int32_t layer, const SeqBatch& b, const int32_t* order,
-                         unsigned long long* err, hipStream_t st)
+                         unsigned long long* err, int32_t max_wgs, hipStream_t st)
 {
     (void)num_layers;
     const uint32_t v = uint32_t(g.row_bytes / unit);
     const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
-    const dim3 grid(uint32_t(b.tile0[b.n]));
+    const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
 #define KVM_UNPACK(U)                                                                       \
     hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dq, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_UNPACK)
@@ -577,11 +599,11 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
 
 hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t layer,
                                const LayerBatch& b, const int32_t* order,
-                               unsigned long long* err, hipStream_t st)
+                               unsigned long long* err, int32_t max_wgs, hipStream_t st)
 {
     const uint32_t v = uint32_t(g.row_bytes / unit);
     const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
-    const dim3 grid(uint32_t(b.tile0[b.n]));
+    const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
 #define KVM_FUSED(U)                                                                        \
     hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, kFusedWaveMajor>), grid,   \
                        dim3(kFusedBS), 0, st, g, pool, layer, b, order, dq, dv, err)
@@ -591,10 +613,10 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
 }
 
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
-                        hipStream_t st)
+                        int32_t max_wgs, hipStream_t st)
 {
     const FastDiv dv = make_fastdiv(uint32_t(row_bytes / unit));
-    const dim3 grid(uint32_t(b.tile0[b.n]));
+    const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
 #define KVM_MERGE(U)                                                                        \
     hipLaunchKernelGGL((k_merge<U, kMergeBS, kMergeUnroll, kMergeWaveMajor>), grid, dim3(kMergeBS), 0, st, rows_per_tile, b, dv)
     KVM_UNIT_SWITCH(unit, KVM_MERGE)

@@ -98,20 +98,23 @@ struct CopyDesc {
 
 // All launches go to `st` and return the launch status. `unit` is the move
 // width in bytes (16, 8, 4, 2 or 1) that divides every address and stride.
+// max_wgs > 0 caps the grid of a tile kernel (each workgroup then loops over
+// tiles i, i + grid, ...); 0 launches one workgroup per tile.
 hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
-                       const SeqBatch& b, unsigned long long* err, hipStream_t st);
+                       const SeqBatch& b, unsigned long long* err, int32_t max_wgs,
+                       hipStream_t st);
 
 // order: a permutation of the batch's tiles (workgroup i takes tile order[i]),
 // made by launch_unpack_order; null keeps the tiles' own order.
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
                          int32_t layer, const SeqBatch& b, const int32_t* order,
-                         unsigned long long* err, hipStream_t st);
+                         unsigned long long* err, int32_t max_wgs, hipStream_t st);
 
 // Hit rows of one layer into the pool slots and into the output rows, one
 // read per row; `order` as for launch_unpack (made from the same tables).
 hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t layer,
                                const LayerBatch& b, const int32_t* order,
-                               unsigned long long* err, hipStream_t st);
+                               unsigned long long* err, int32_t max_wgs, hipStream_t st);
 
 // Sort the batch's unpack tiles by destination block id into `order`
 // (b.tile0[b.n] entries). count_scratch holds 2 * (num_blocks + 2) words.
@@ -119,7 +122,7 @@ hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* 
                                int32_t* order, hipStream_t st);
 
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
-                        hipStream_t st);
+                        int32_t max_wgs, hipStream_t st);
 
 // group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1.
 hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uint64_t src_bytes,

@@ -70,6 +70,7 @@ SIGNATURES = {
     "kvm_create": ([ctypes.c_int, ctypes.POINTER(_P)], ctypes.c_int),
     "kvm_destroy": ([_P], None),
     "kvm_ctx_reserve": ([_P, _I64, _I64], ctypes.c_int),
+    "kvm_ctx_set_max_workgroups": ([_P, _I32], ctypes.c_int),
     "kvm_ctx_last_error": ([_P], ctypes.c_char_p),
     "kvm_take_device_errors": ([_P, ctypes.POINTER(_I64)], ctypes.c_int),
     "kvm_pack_full": ([_P, ctypes.POINTER(kvm_pool_layout), _P, _I32, ctypes.POINTER(kvm_seq),
@@ -152,6 +153,10 @@ def kvm_destroy(ctx: int) -> None:
 
 def kvm_ctx_reserve(ctx: int, max_seqs: int, max_descs: int) -> None:
     _check("kvm_ctx_reserve", load().kvm_ctx_reserve(ctx, max_seqs, max_descs), ctx)
+
+
+def kvm_ctx_set_max_workgroups(ctx: int, max_workgroups: int) -> None:
+    _check("kvm_ctx_set_max_workgroups", load().kvm_ctx_set_max_workgroups(ctx, max_workgroups), ctx)
 
 
 def kvm_ctx_last_error(ctx: int) -> str:
@@ -255,6 +260,9 @@ class Context:
 
     def reserve(self, max_seqs: int, max_descs: int):
         kvm_ctx_reserve(self.handle, max_seqs, max_descs)
+
+    def set_max_workgroups(self, max_workgroups: int):
+        kvm_ctx_set_max_workgroups(self.handle, max_workgroups)
 
     def take_device_errors(self) -> int:
         return kvm_take_device_errors(self.handle)
