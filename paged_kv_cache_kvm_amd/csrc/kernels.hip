@@ -103,6 +103,58 @@ __device__ __forceinline__ bool bad_block(int32_t blk, int64_t num_blocks)
     return blk < 0 || int64_t(blk) >= num_blocks;
 }
 
+// A tile of a batch whose records carry block tables: its record si, the
+// block-table entry b it covers, the block id found there, and (pack only)
+// the layer l. per = tiles per block-table entry (L for pack, 1 for unpack).
+struct TileAt {
+    int32_t si;
+    int32_t l;
+    int64_t b;
+    int32_t blk;
+};
+
+template <class Batch>
+__device__ __forceinline__ TileAt tile_at(const Batch& batch, int32_t per, int64_t tile)
+{
+    TileAt t;
+    t.si = find_record(batch.tile0, batch.n, tile);
+    const int64_t rem = tile - batch.tile0[t.si];
+    t.b = per == 1 ? rem : rem / per;
+    t.l = int32_t(rem - t.b * per);
+    t.blk = batch.rec[t.si].block_table[t.b];
+    return t;
+}
+
+// Workgroup blockIdx.x takes tiles order[i] for i = blockIdx.x, + grid, ...
+// (a null order means tile i). Under a workgroup budget one workgroup copies
+// many tiles in turn, so the next tile's record and block id are fetched
+// before the current tile is copied, and the order entry one tile further
+// ahead: the dependent metadata loads then overlap a copy instead of sitting
+// between two. With one workgroup per tile the loop body runs once.
+template <class Batch, class Body>
+__device__ __forceinline__ void walk_tiles(const Batch& batch, int32_t per,
+                                           const int32_t* __restrict__ order, Body body)
+{
+    const int64_t n = batch.tile0[batch.n];
+    const int64_t grid = gridDim.x;
+    int64_t i = blockIdx.x;
+    if (i >= n) return;
+    TileAt cur = tile_at(batch, per, order ? int64_t(order[i]) : i);
+    int64_t next = i + grid < n ? (order ? int64_t(order[i + grid]) : i + grid) : 0;
+    for (;;) {
+        const bool more = i + grid < n;
+        TileAt nxt = cur;
+        if (more) nxt = tile_at(batch, per, next);
+        const int64_t j = i + 2 * grid;
+        const int64_t after = j < n ? (order ? int64_t(order[j]) : j) : 0;
+        body(cur);
+        if (!more) break;
+        cur = nxt;
+        next = after;
+        i += grid;
+    }
+}
+
 // Copy the `total` unit-sized elements of one tile with a workgroup of BS
 // threads: every thread issues UNR loads, then UNR stores, so a workgroup keeps
 // BS*UNR*U bytes in flight. addr(j, src, dst) names element j's two addresses;
@@ -166,17 +218,14 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
                                              FastDiv div_q, FastDiv div_v,
                                              unsigned long long* err)
 {
-    const int64_t ntiles = batch.tile0[batch.n];
-    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int32_t si = find_record(batch.tile0, batch.n, tile);
-        const SeqRec s = batch.rec[si];
-        const int64_t rem = tile - batch.tile0[si];
-        const int64_t b = rem / num_layers;
-        const int32_t l = int32_t(rem - b * num_layers);
-        const int32_t blk = s.block_table[b];
+    walk_tiles(batch, num_layers, nullptr, [&](const TileAt& t) {
+        const SeqRec& s = batch.rec[t.si];
+        const int64_t b = t.b;
+        const int32_t l = t.l;
+        const int32_t blk = t.blk;
         if (bad_block(blk, g.num_blocks)) {
             if (threadIdx.x == 0) atomicAdd(err, 1ull);
-            continue;
+            return;
         }
         const int64_t t0 = b * g.block_tokens;
         const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
@@ -191,7 +240,7 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
             sp = src + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
             dp = dst + int64_t(r) * s.token_stride + int64_t(q) * U;
         });
-    }
+    });
 }
 
 // -------------------------------------------------------------- unpack ---
@@ -206,16 +255,13 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
                                                FastDiv div_q, FastDiv div_v,
                                                unsigned long long* err)
 {
-    const int64_t ntiles = batch.tile0[batch.n];
-    for (int64_t i = blockIdx.x; i < ntiles; i += gridDim.x) {
-        const int64_t tile = order ? order[i] : i;
-        const int32_t si = find_record(batch.tile0, batch.n, tile);
-        const SeqRec s = batch.rec[si];
-        const int64_t b = tile - batch.tile0[si];
-        const int32_t blk = s.block_table[b];
+    walk_tiles(batch, 1, order, [&](const TileAt& t) {
+        const SeqRec& s = batch.rec[t.si];
+        const int64_t b = t.b;
+        const int32_t blk = t.blk;
         if (bad_block(blk, g.num_blocks)) {
             if (threadIdx.x == 0) atomicAdd(err, 1ull);
-            continue;
+            return;
         }
         const int64_t t0 = b * g.block_tokens;
         const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
@@ -229,7 +275,7 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
             sp = src + int64_t(r) * s.token_stride + int64_t(q) * U;
             dp = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
         });
-    }
+    });
 }
 
 // ---------------------------------------------------- unpack + merge ---
@@ -245,16 +291,13 @@ __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restric
                                                      unsigned long long* err)
 {
     typedef typename Unit<U>::T V;
-    const int64_t ntiles = batch.tile0[batch.n];
-    for (int64_t i = blockIdx.x; i < ntiles; i += gridDim.x) {
-        const int64_t tile = order ? order[i] : i;
-        const int32_t si = find_record(batch.tile0, batch.n, tile);
-        const LayerRec s = batch.rec[si];
-        const int64_t b = tile - batch.tile0[si];
-        const int32_t blk = s.block_table[b];
+    walk_tiles(batch, 1, order, [&](const TileAt& t) {
+        const LayerRec& s = batch.rec[t.si];
+        const int64_t b = t.b;
+        const int32_t blk = t.blk;
         if (bad_block(blk, g.num_blocks)) {
             if (threadIdx.x == 0) atomicAdd(err, 1ull);
-            continue;
+            return;
         }
         const int64_t t0 = b * g.block_tokens;
         const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
@@ -292,7 +335,7 @@ __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restric
                 }
             }
         }
-    }
+    });
 }
 
 // --------------------------------------------------------------- merge ---
