@@ -180,7 +180,9 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
  * previous layer's compute on another stream (DualPath KV Loading, layerwise
  * Prefill; Tutti reading notes, design 2: I/O kernels kept to a few SMs
  * beside compute). The bytes written are the same for every budget.
- * 0 (the default) means one workgroup per tile. The destination-order sort
+ * 0 (the default) keeps the library's own grids: one workgroup per tile for
+ * pack, unpack and the fused call, at most 16 workgroups per CU for merge and
+ * 8 per CU for the batched copy. The destination-order sort
  * that unpack runs once per new set of block tables is not bounded (it
  * touches 8 bytes per tile). Applies to calls enqueued
  * after it returns; calls already enqueued keep their grids. Errors:

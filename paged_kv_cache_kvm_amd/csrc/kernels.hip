@@ -16,8 +16,10 @@
 //                       1152-byte MLA row or a 256-byte tiny row keeps all 256
 //                       lanes busy; element -> (row, side, column) uses
 //                       multiply-high division by invariant integers.
-//   k_merge             one workgroup per (request, chunk of rows); a row comes
-//                       from the strided hit slice or from the miss rows.
+//   k_merge             a tile is (request, chunk of rows); a row comes from
+//                       the strided hit slice or from the miss rows. The grid
+//                       is capped (16 workgroups per CU), and each workgroup
+//                       walks tiles i, i + grid, ...
 //   k_bc_*              batched copy: per-group byte sums (64 objects per
 //                       wavefront), one exclusive scan, then a fixed grid in
 //                       which every wavefront copies an equal share of the
