@@ -44,7 +44,10 @@
  *     void*; NULL is the null stream). KVM_OK means "enqueued"; the result is
  *     there once the stream (or an event recorded after the call) completes.
  *   - Every argument is validated before anything is enqueued: a call that
- *     returns an error has enqueued nothing and written nothing.
+ *     returns KVM_EINVAL or KVM_ERANGE has enqueued nothing. One that returns
+ *     KVM_ENOMEM has written no caller buffer (only the library's own scratch
+ *     may have been). A KVM_EHIP from a failed launch can leave the call's
+ *     earlier launches (its first records) enqueued.
  *   - Payload is opaque bytes: no value is converted, so bf16 NaN payloads,
  *     -0 and denormals move bit for bit.
  *   - Any byte alignment is accepted. Pointers, strides and row sizes that are

@@ -228,8 +228,9 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     OrderSlot* o = &c->orders[0];
     for (OrderSlot& x : c->orders)
         if (x.used < o->used) o = &x;
-    if (o->valid) {  // its order may still be read by an unpack in flight
-        hipError_t e = hipEventSynchronize(o->last_use);
+    if (o->valid) {  // its sort or an unpack reading it may still be in flight
+        hipError_t e = hipEventSynchronize(o->ready);
+        if (e == hipSuccess) e = hipEventSynchronize(o->last_use);
         if (e != hipSuccess) return fail_hip(c, e, "hipEventSynchronize");
         o->valid = false;
     }
