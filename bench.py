@@ -66,8 +66,20 @@ class Events:
         e1.record()
         self.pairs.setdefault(name, []).append((e0, e1))
 
+    def all_ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs[name]]
+
     def mean_ms(self, name):
-        return statistics.fmean(a.elapsed_time(b) for a, b in self.pairs[name])
+        return statistics.fmean(self.all_ms(name))
+
+
+def quantile(xs, q):
+    """Linear-interpolated quantile of a non-empty list."""
+    xs = sorted(xs)
+    pos = q * (len(xs) - 1)
+    lo = int(pos)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (pos - lo)
 
 
 def llama_setup(torch, kv, wl, dev):
@@ -334,22 +346,31 @@ def pipeline_section(torch, kv, ctx, s, reps=3, d_model=4096, d_ff=14336):
             "overlapped_by_workgroup_budget": over}
 
 
-def copy_ceiling(torch, dev, nbytes=2 << 30, reps=10):
-    """Device-to-device copy of nbytes through torch (hipMemcpy), read+write GB/s."""
+def copy_ceilings(torch, kv, ctx, dev, nbytes=2 << 30, reps=10):
+    """Two device-to-device copies of nbytes, read+write GB/s: torch's copy
+    (the runtime's blit kernel), and a plain 16-byte streaming copy through
+    this library (kvm_batch_copy of one nbytes object)."""
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     a.fill_(1)
-    for _ in range(2):
-        b.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    desc = torch.tensor([0, 0, nbytes], dtype=torch.int64, device=dev)
+
+    def rate(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 2 * nbytes / (e0.elapsed_time(e1) / reps * 1e6)
+
+    torch_copy = rate(lambda: b.copy_(a))
+    stream_copy = rate(lambda: kv.kvm_batch_copy(ctx.handle, b, nbytes, a, nbytes, desc, 1))
+    assert ctx.take_device_errors() == 0
     del a, b
-    return 2 * nbytes / (ms * 1e6)
+    return torch_copy, stream_copy
 
 
 def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
@@ -381,7 +402,20 @@ def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
             "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
 
 
-def cpu_baseline(wl, reps=3):
+def host_cpu():
+    """The host CPU's model name and the hardware threads this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, reps=12):
     """The oracle on the host cores, on request 0 of the same workload: its 32
     unpack_layer + merge_layer calls and its pack_full (1/8 of a step). The
     request's 2080 blocks sit in a host pool of exactly that many blocks under
@@ -418,10 +452,12 @@ def cpu_baseline(wl, reps=3):
         times.append(time.perf_counter() - t0)
     dt = statistics.median(times)
     nbytes = L * 2 * t_hit * C + L * 2 * t_all * C + 2 * t_all * L * C
+    model, threads = host_cpu()
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"request 0 of 8 ({L} unpack_layer + {L} merge_layer + pack_full, "
                       f"{nbytes / 1e9:.1f} GB), median of {reps} runs ({sum(times):.1f} s), "
-                      f"single thread, host pool of the request's {N} blocks"}
+                      f"single thread, host pool of the request's {N} blocks",
+            "host": f"{model}; {threads} hardware threads available"}
 
 
 PROFILE = os.path.join(ROOT, "profiles", "llama8b_layer_loop_hbm_traffic.md")
@@ -480,7 +516,7 @@ def main():
     # each op alone (its launches back to back), divided by the launch count
     ev = Events(torch)
     L = s["L"]
-    for _ in range(max(3, args.steps // 2)):
+    for _ in range(max(5, args.steps)):
         ev.around("unpack_layer", lambda: [kv.kvm_unpack_layer(
             ctx.handle, s["layout"], s["pool"], L, l, s["unpack_seqs"]) for l in range(L)])
         ev.around("merge_layer", lambda: [kv.kvm_merge_layer(
@@ -490,10 +526,14 @@ def main():
     torch.cuda.synchronize()
     ops = {}
     for name in ("unpack_layer", "merge_layer", "pack_full"):
-        ms = ev.mean_ms(name) / s["launches"][name]
+        per_launch = [t / s["launches"][name] for t in ev.all_ms(name)]
+        ms = statistics.fmean(per_launch)
         gbs = s["bytes"][name] / (ms * 1e6)
         ops[name] = {"launches_per_step": s["launches"][name],
                      "bytes_per_launch": s["bytes"][name], "ms_per_launch": round(ms, 4),
+                     "ms_per_launch_p10_p50_p90": [round(quantile(per_launch, q), 4)
+                                                   for q in (0.1, 0.5, 0.9)],
+                     "repetitions": len(per_launch),
                      "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
     dom = max(ops, key=lambda k: ops[k]["ms_per_launch"] * ops[k]["launches_per_step"])
     fused = fused_section(torch, kv, ctx, s, args.steps, args.warmup, step_bytes, ms_step)
@@ -504,7 +544,9 @@ def main():
     del s
     torch.cuda.empty_cache()
 
-    ceiling = copy_ceiling(torch, dev)
+    ceiling, stream_copy = copy_ceilings(torch, kv, ctx, dev)
+    for v in ops.values():
+        v["pct_of_copy_ceiling"] = round(100 * v["GBps"] / max(ceiling, stream_copy), 1)
     bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
@@ -531,6 +573,7 @@ def main():
         "host_tier": host,
         "pipeline": pipe,
         "copy_ceiling_GBps": round(ceiling, 1),
+        "stream_copy_GBps": round(stream_copy, 1),
         "batch_copy": bc,
         "cpu_baseline": cpu,
     }
