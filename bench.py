@@ -402,6 +402,52 @@ def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
             "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
 
 
+def restore_section(torch, kv, wl, ctx, dev, reps=10):
+    """The long-sequence restore list (one 128,000-token sequence of a
+    Qwen3-32B-like model, L=64, B=64: 256,000 K/V objects of 128 KiB from
+    random staging offsets into their paged slots), as one batched copy and as
+    one call per layer (4,000 objects each)."""
+    descs_np, _, pool_bytes = wl.qwen32b_object_descs()
+    n, L = len(descs_np), wl.QWEN32B_SHAPE.layers
+    total = int(descs_np[:, 2].sum())
+    log(f"[bench] restore: {n} objects of 128 KiB, {total / 1e9:.2f} GB each way")
+    u8 = dict(dtype=torch.uint8, device=dev)
+    staging = torch.empty(wl.QWEN32B_STAGING, **u8)
+    wl.fill_random_bytes_(staging, 1003, 3)
+    pool = torch.empty(pool_bytes, **u8)
+    descs = torch.from_numpy(descs_np.view(__import__("numpy").uint8).reshape(-1)).to(dev)
+    per = n // L
+    ctx.reserve(64, n)
+
+    def one_call():
+        kv.kvm_batch_copy(ctx.handle, pool, pool_bytes, staging, wl.QWEN32B_STAGING, descs, n)
+
+    def per_layer():
+        for l in range(L):
+            kv.kvm_batch_copy(ctx.handle, pool, pool_bytes, staging, wl.QWEN32B_STAGING,
+                              descs.data_ptr() + l * per * 24, per)
+
+    out = {"workload": f"restore list: {n} objects x 128 KiB (L={L}, 2000 blocks, K and V)",
+           "bytes_rw": 2 * total}
+    ev = Events(torch)
+    for name, fn in (("one_call", one_call), ("per_layer_calls", per_layer)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            ev.around(name, fn)
+        torch.cuda.synchronize()
+        ms = ev.mean_ms(name)
+        gbs = 2 * total / (ms * 1e6)
+        out[name] = {"ms": round(ms, 4), "GBps": round(gbs, 1),
+                     "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                     "descriptors_per_s": round(n / (ms * 1e-3), 0)}
+    assert ctx.take_device_errors() == 0
+    del staging, pool, descs
+    torch.cuda.empty_cache()
+    return out
+
+
 def host_cpu():
     """The host CPU's model name and the hardware threads this process may use."""
     model = "unknown"
@@ -548,6 +594,7 @@ def main():
     for v in ops.values():
         v["pct_of_copy_ceiling"] = round(100 * v["GBps"] / max(ceiling, stream_copy), 1)
     bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
+    restore = None if args.no_batch_copy else restore_section(torch, kv, wl, ctx, dev)
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
 
@@ -575,6 +622,7 @@ def main():
         "copy_ceiling_GBps": round(ceiling, 1),
         "stream_copy_GBps": round(stream_copy, 1),
         "batch_copy": bc,
+        "batch_copy_restore": restore,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
