@@ -12,12 +12,14 @@ Also reported: each op's average launch time from HIP events on the launch
 stream, the roofline of the dominant kernel, the same step with unpack and
 merge fused per layer (kvm_unpack_merge_layer), the host tier (a pinned host
 Full Block / complete_layer over PCIe), the layerwise overlap of the moves
-with a stand-in compute stream under workgroup budgets, a device copy ceiling, the
-small-object batched copy (200000 objects of 256*U{16..512} bytes) and the
-oracle timed on the host cores on one request of the same workload.
+with a stand-in compute stream under workgroup budgets, two device copy
+ceilings, the MLA agentic layer loop (61 layers, 576-element latent, 64
+requests), the small-object batched copy (200000 objects of 256*U{16..512}
+bytes), the 256,000-object restore list, and the oracle timed on the host
+cores on one request of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-batch-copy]
-                      [--no-host] [--no-pipeline]
+                      [--no-host] [--no-pipeline] [--no-mla]
 """
 from __future__ import annotations
 
@@ -46,6 +48,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-batch-copy", action="store_true", help="skip the batched-copy section")
     ap.add_argument("--no-host", action="store_true", help="skip the pinned-host-buffer section")
+    ap.add_argument("--no-mla", action="store_true", help="skip the MLA agentic layer loop")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the layerwise overlap section (workgroup-bounded moves)")
     return ap.parse_args()
@@ -402,6 +405,80 @@ def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
             "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
 
 
+def mla_section(torch, kv, wl, ctx, dev, reps=3):
+    """The MLA agentic layer loop (64 requests, T_hit ~ U{16384..65536},
+    T_miss ~ U{128..1024}, 61 layers of one 576-element bf16 latent, B=64, a
+    one-layer slot pool): per layer unpack + merge into a 2-deep complete_layer
+    ring, and the same loop with the fused call."""
+    w = wl.mla_agentic()
+    sh = w.shape
+    L, S, B, rb, C = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, sh.c_kv_bytes
+    R = len(w.t_hit)
+    per_req = [wl.blocks_needed(t, B) for t in w.t_all]
+    N = sum(per_req)
+    miss_all = sum(w.t_miss) * C
+    ring_bytes = sum(w.t_all) * C
+    need = sum(w.t_hit) * L * C + L * miss_all + N * B * rb + 2 * ring_bytes
+    free, _ = torch.cuda.mem_get_info(dev)
+    log(f"[bench] {w.name}: allocating {need / 2**30:.1f} GiB of {free / 2**30:.1f} GiB free")
+    if need + (2 << 30) > free:
+        return {"workload": w.name, "skipped": f"needs {need} bytes, {free} free"}
+    u8 = dict(dtype=torch.uint8, device=dev)
+    bts = [torch.from_numpy(t).to(dev) for t in wl.block_tables(w.seed, 2, N, per_req)]
+    fbs = []
+    for r in range(R):
+        fbs.append(torch.empty(w.t_hit[r] * L * C, **u8))
+        wl.fill_bf16_normal_(fbs[r], w.seed, 100 + r)
+    misses = torch.empty(L * miss_all, **u8)                  # [L][request][T_miss][C]
+    wl.fill_bf16_normal_(misses, w.seed, 7)
+    slot = torch.empty(N * B * rb, **u8)
+    rings = [torch.empty(ring_bytes, **u8) for _ in range(2)]
+    moff, roff = [0], [0]
+    for r in range(R):
+        moff.append(moff[-1] + w.t_miss[r] * C)
+        roff.append(roff[-1] + w.t_all[r] * C)
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, 0, N)
+    seqs = [kv.seq(bts[r], fbs[r], w.t_hit[r]) for r in range(R)]
+    merge_l, fused_l = [], []
+    for l in range(L):
+        mbase = misses.data_ptr() + l * miss_all
+        out = rings[l % 2].data_ptr()
+        merge_l.append([kv.merge_seq(fbs[r].data_ptr() + l * C, L * C, w.t_hit[r],
+                                     mbase + moff[r], C, w.t_miss[r], out + roff[r], C)
+                        for r in range(R)])
+        fused_l.append([kv.layer_seq(bts[r], fbs[r], w.t_hit[r], mbase + moff[r], C,
+                                     w.t_miss[r], out + roff[r], C) for r in range(R)])
+
+    def separate():
+        for l in range(L):
+            kv.kvm_unpack_layer(ctx.handle, layout, slot, L, l, seqs)
+            kv.kvm_merge_layer(ctx.handle, C, merge_l[l])
+
+    def fused():
+        for l in range(L):
+            kv.kvm_unpack_merge_layer(ctx.handle, layout, slot, L, l, fused_l[l])
+
+    th, ta, tm = sum(w.t_hit), sum(w.t_all), sum(w.t_miss)
+    bytes_sep = L * (2 * th * C + 2 * ta * C)
+    bytes_fused = L * (3 * th + 2 * tm) * C
+    ev = Events(torch)
+    out = {"workload": w.name, "sum_t_hit": th, "sum_t_miss": tm}
+    for name, fn, nbytes in (("separate", separate, bytes_sep), ("fused", fused, bytes_fused)):
+        fn()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            ev.around(name, fn)
+        torch.cuda.synchronize()
+        ms = ev.mean_ms(name)
+        out[name] = {"ms_per_loop": round(ms, 3), "bytes_per_loop": nbytes,
+                     "GBps": round(nbytes / (ms * 1e6), 1),
+                     "pct_hbm_peak": round(100 * nbytes / (ms * 1e6) / HBM_PEAK_GBS, 2)}
+    assert ctx.take_device_errors() == 0
+    del fbs, misses, slot, rings, bts
+    torch.cuda.empty_cache()
+    return out
+
+
 def restore_section(torch, kv, wl, ctx, dev, reps=10):
     """The long-sequence restore list (one 128,000-token sequence of a
     Qwen3-32B-like model, L=64, B=64: 256,000 K/V objects of 128 KiB from
@@ -593,6 +670,7 @@ def main():
     ceiling, stream_copy = copy_ceilings(torch, kv, ctx, dev)
     for v in ops.values():
         v["pct_of_copy_ceiling"] = round(100 * v["GBps"] / max(ceiling, stream_copy), 1)
+    mla = None if args.no_mla else mla_section(torch, kv, wl, ctx, dev)
     bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
     restore = None if args.no_batch_copy else restore_section(torch, kv, wl, ctx, dev)
     ctx.close()
@@ -621,6 +699,7 @@ def main():
         "pipeline": pipe,
         "copy_ceiling_GBps": round(ceiling, 1),
         "stream_copy_GBps": round(stream_copy, 1),
+        "mla_layer_loop": mla,
         "batch_copy": bc,
         "batch_copy_restore": restore,
         "cpu_baseline": cpu,
