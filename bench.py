@@ -20,6 +20,7 @@ cores on one request of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-batch-copy]
                       [--no-host] [--no-pipeline] [--no-mla]
+                      [--no-restore]
 """
 from __future__ import annotations
 
@@ -49,6 +50,8 @@ def parse():
     ap.add_argument("--no-batch-copy", action="store_true", help="skip the batched-copy section")
     ap.add_argument("--no-host", action="store_true", help="skip the pinned-host-buffer section")
     ap.add_argument("--no-mla", action="store_true", help="skip the MLA agentic layer loop")
+    ap.add_argument("--no-restore", action="store_true",
+                    help="skip the 256,000-object restore list")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the layerwise overlap section (workgroup-bounded moves)")
     return ap.parse_args()
@@ -672,7 +675,8 @@ def main():
         v["pct_of_copy_ceiling"] = round(100 * v["GBps"] / max(ceiling, stream_copy), 1)
     mla = None if args.no_mla else mla_section(torch, kv, wl, ctx, dev)
     bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
-    restore = None if args.no_batch_copy else restore_section(torch, kv, wl, ctx, dev)
+    restore = None if args.no_batch_copy or args.no_restore else \
+        restore_section(torch, kv, wl, ctx, dev)
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
 

@@ -199,15 +199,18 @@ __device__ __forceinline__ void copy_elements(uint32_t total, Addr addr)
 // variants timed in one process on the same buffers, interleaved): pack and
 // merge keep a whole 64 KiB tile in flight per workgroup, pack in wave-major
 // order (+2.4 % over thread-major), merge in thread-major order (wave-major
-// costs it 18 %); unpack, whose stores land on scattered pool objects, does
-// best with half a tile in flight and no occupancy cap.
+// costs it 18 %). Unpack, whose stores land on scattered pool objects, and
+// the fused kernel take 576 threads x 8 units (72 KiB in flight, one 64-row
+// MLA tile of 1152-byte rows exactly): against 256 x 8 that moves 1-1.6 %
+// more on the Llama layer loop and 3 % more on the MLA loop, where 512 x 8
+// gains only on MLA. No occupancy cap helps unpack.
 constexpr int kPackBS = 1024, kPackUnroll = 4;
 constexpr bool kPackWaveMajor = true;
 constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
-constexpr int kUnpackBS = 256, kUnpackUnroll = 8;
+constexpr int kUnpackBS = 576, kUnpackUnroll = 8;
 constexpr bool kUnpackWaveMajor = false;
-constexpr int kFusedBS = 256, kFusedUnroll = 8;
+constexpr int kFusedBS = 576, kFusedUnroll = 8;
 constexpr bool kFusedWaveMajor = false;
 
 // ---------------------------------------------------------------- pack ---
