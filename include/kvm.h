@@ -281,8 +281,9 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
  * descs is a DEVICE array of n_descs kvm_copy_desc. dst_bytes and src_bytes are
  * the sizes of the two buffers; an object outside its buffer is skipped and
  * counted (kvm_take_device_errors). Zero-length objects are no-ops. The bytes
- * are split evenly over the device's wavefronts, so a few large objects and
- * many small ones balance alike. dst_base and src_base may be the same
+ * are split evenly over the device's wavefronts (8 workgroups per CU, or 2
+ * when the objects average 64 KiB or more and the call moves 1 GiB or more),
+ * so a few large objects and many small ones balance alike. dst_base and src_base may be the same
  * buffer. Errors: KVM_EINVAL (null ctx, null descs/bases with n_descs > 0,
  * n_descs < 0), KVM_ERANGE (n_descs above 2^32), KVM_ENOMEM, KVM_EHIP. */
 int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,

@@ -647,8 +647,10 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     if (rc != KVM_OK) return rc;
     // Enough wavefronts to cover every CU several times over, or the
     // workgroup budget if smaller; each takes an equal share of the bytes.
+    // Lists of large objects use 2 workgroups per CU (within the budget).
     const int32_t copy_blocks =
         ctx->max_wgs > 0 ? std::min(ctx->max_wgs, ctx->num_cus * 8) : ctx->num_cus * 8;
+    const int32_t large_blocks = std::min(copy_blocks, ctx->num_cus * 2);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (ctx->copy_pending && ctx->copy_stream != st) {
@@ -658,7 +660,7 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     e = kvm::launch_batch_copy(
         static_cast<char*>(dst_base), dst_bytes, static_cast<const char*>(src_base), src_bytes,
         reinterpret_cast<const CopyDesc*>(descs), n_descs, ctx->d_groups,
-        ctx->d_groups + ctx->group_cap, copy_blocks, ctx->d_err, st);
+        ctx->d_groups + ctx->group_cap, copy_blocks, large_blocks, ctx->d_err, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "batch copy launch");
     e = hipEventRecord(ctx->copy_done, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "hipEventRecord");

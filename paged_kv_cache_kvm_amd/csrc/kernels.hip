@@ -529,16 +529,29 @@ __device__ __forceinline__ void wave_copy(const char* __restrict__ s, char* __re
 // over groups, then a scan across the 64 lanes of that group), then walks the
 // objects in order until its share is done. An object larger than Q is split
 // across wavefronts; many small objects go to one wavefront.
+//
+// When the objects average at least kLargeObject bytes and the call moves at
+// least kLargeCall bytes, only the first large_waves wavefronts take shares
+// (the rest exit at once). Measured on MI355X, 2 workgroups per CU instead of
+// 8 move a 33.5 GB list of 128 KiB objects 5.5 % faster and one 2 GiB object
+// 3-4 % faster; a 0.5 GB call loses 4 % that way, and lists of small
+// objects, which are bound by walking descriptors, need every wavefront.
+constexpr uint64_t kLargeObject = 64 * 1024;
+constexpr uint64_t kLargeCall = uint64_t(1) << 30;
 __global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__ descs, int64_t n,
                                                     const char* __restrict__ src,
                                                     uint64_t src_bytes, char* __restrict__ dst,
                                                     uint64_t dst_bytes,
                                                     const uint64_t* __restrict__ group_base,
-                                                    int64_t ngroups)
+                                                    int64_t ngroups, uint64_t large_waves)
 {
     const int lane = threadIdx.x & 63;
     const uint64_t total = group_base[ngroups];
-    const uint64_t nwaves = uint64_t(gridDim.x) * kWavesPerBlock;
+    const uint64_t all_waves = uint64_t(gridDim.x) * kWavesPerBlock;
+    const uint64_t nwaves =
+        total >= uint64_t(n) * kLargeObject && total >= kLargeCall
+            ? max(uint64_t(1), min(large_waves, all_waves))
+            : all_waves;
     const uint64_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
     uint64_t share = (total + nwaves - 1) / nwaves;
     share = (share + 4095) & ~uint64_t(4095);
@@ -674,8 +687,8 @@ hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, cons
 
 hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uint64_t src_bytes,
                              const CopyDesc* descs, int64_t n, uint64_t* group_sum,
-                             uint64_t* group_base, int32_t copy_blocks, unsigned long long* err,
-                             hipStream_t st)
+                             uint64_t* group_base, int32_t copy_blocks, int32_t large_blocks,
+                             unsigned long long* err, hipStream_t st)
 {
     const int64_t ng = (n + kDescGroup - 1) / kDescGroup;
     const uint32_t sum_blocks = uint32_t((ng + kWavesPerBlock - 1) / kWavesPerBlock);
@@ -685,7 +698,8 @@ hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uin
                        reinterpret_cast<const unsigned long long*>(group_sum),
                        reinterpret_cast<unsigned long long*>(group_base), ng);
     hipLaunchKernelGGL(k_bc_copy, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs, n, src,
-                       src_bytes, dst, dst_bytes, group_base, ng);
+                       src_bytes, dst, dst_bytes, group_base, ng,
+                       uint64_t(large_blocks) * kWavesPerBlock);
     return hipGetLastError();
 }
 
