@@ -183,8 +183,8 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
  * previous layer's compute on another stream (DualPath KV Loading, layerwise
  * Prefill; Tutti reading notes, design 2: I/O kernels kept to a few SMs
  * beside compute). The bytes written are the same for every budget.
- * 0 (the default) keeps the library's own grids: one workgroup per tile for
- * pack, unpack and the fused call, at most 16 workgroups per CU for merge and
+ * 0 (the default) keeps the library's own grids: one workgroup per work item
+ * for pack, unpack and the fused call, at most 16 workgroups per CU for merge and
  * 8 per CU for the batched copy. The destination-order sort
  * that unpack runs once per new set of block tables is not bounded (it
  * touches 8 bytes per tile). Applies to calls enqueued
@@ -209,7 +209,7 @@ int kvm_take_device_errors(kvm_ctx* ctx, int64_t* count);
  * Errors: KVM_EINVAL (null ctx/layout/pool/seqs with n > 0, a sequence with
  * null pointers and num_tokens > 0, bad layout or strides, n < 0,
  * num_layers < 1), KVM_ERANGE (n above 2^20, a tile above 2^31 bytes or
- * 2^31 tiles), KVM_ENOMEM, KVM_EHIP. */
+ * 2^31 work items in one launch), KVM_ENOMEM, KVM_EHIP. */
 int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
                   int32_t num_layers, const kvm_seq* seqs, int32_t n, void* stream);
 
@@ -219,7 +219,8 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  *     pool[layer][s][block_table[t / B]][t % B] <- full[t][layer][s]  (row_bytes)
  * Slot rows of tokens >= num_tokens (a partial last block shared with miss
  * tokens) are left as they were. One launch per 128 sequences; one workgroup
- * per (sequence, block) tile. Tiles run in ascending destination-block order:
+ * per (sequence, block, side) work item. Blocks run in ascending
+ * destination-block order:
  * the first call with a given set of sequence records sorts them on the
  * stream (a counting sort over the pool's blocks, kept in the context for the
  * following layers; skipped when the pool has far more blocks than the call

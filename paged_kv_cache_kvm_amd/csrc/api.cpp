@@ -169,7 +169,9 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
             std::memset(&nb_, 0, sizeof(nb_));
         }
         kvm::SeqBatch& b = plan->batches.back();
-        if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
+        // unpack launches one work item per (tile, side)
+        const int64_t items_per_tile = per_layer_tiles ? 1 : p->num_sides;
+        if ((b.tile0[b.n] + tiles) * items_per_tile > kMaxTiles) return KVM_ERANGE;
         b.rec[b.n].block_table = s.block_table;
         b.rec[b.n].full = static_cast<const char*>(s.full);
         b.rec[b.n].num_tokens = s.num_tokens;
@@ -598,7 +600,7 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
         kvm::LayerBatch& b = hit.back();
         kvm::SeqBatch& k = keys.back();
         const int64_t tiles = (s.t_hit + layout->block_tokens - 1) / layout->block_tokens;
-        if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
+        if ((b.tile0[b.n] + tiles) * layout->num_sides > kMaxTiles) return KVM_ERANGE;
         b.rec[b.n] = {s.block_table, static_cast<const char*>(s.full), s.t_hit, ts,
                       static_cast<char*>(s.out), s.out_stride};
         k.rec[k.n] = {s.block_table, static_cast<const char*>(s.full), s.t_hit, ts};

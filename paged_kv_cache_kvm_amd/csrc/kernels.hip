@@ -5,17 +5,18 @@
 // in flight per CU, keeping every lane busy on ragged rows, and never writing
 // a partial cache line that a full row would cover:
 //
-//   k_pack / k_unpack   one workgroup per tile. A pack tile is (sequence,
-//                       block, layer); an unpack tile is (sequence, block).
-//                       With a workgroup budget below the tile count, the
-//                       grid is the budget and workgroup i takes tiles i,
+//   k_pack / k_unpack   one workgroup per work item. A pack item is
+//                       (sequence, block, layer); an unpack item is
+//                       (sequence, block, side).
+//                       With a workgroup budget below the item count, the
+//                       grid is the budget and workgroup i takes items i,
 //                       i + grid, i + 2*grid, ... (this bounds how many CUs
 //                       the moves occupy while other work shares the GPU).
-//                       A tile's rows (B tokens x sides) are flattened into
-//                       one index space of `unit`-byte elements so that a
-//                       1152-byte MLA row or a 256-byte tiny row keeps all 256
-//                       lanes busy; element -> (row, side, column) uses
-//                       multiply-high division by invariant integers.
+//                       An item's rows are flattened into one index space of
+//                       `unit`-byte elements so that a 1152-byte MLA row or a
+//                       256-byte tiny row keeps every lane busy; element ->
+//                       (row, side, column) uses multiply-high division by
+//                       invariant integers.
 //   k_merge             a tile is (request, chunk of rows); a row comes from
 //                       the strided hit slice or from the miss rows. The grid
 //                       is capped (16 workgroups per CU), and each workgroup
@@ -105,50 +106,62 @@ __device__ __forceinline__ bool bad_block(int32_t blk, int64_t num_blocks)
     return blk < 0 || int64_t(blk) >= num_blocks;
 }
 
-// A tile of a batch whose records carry block tables: its record si, the
-// block-table entry b it covers, the block id found there, and (pack only)
-// the layer l. per = tiles per block-table entry (L for pack, 1 for unpack).
+// A work item of a batch whose records carry block tables: its record si,
+// the block-table entry b it covers, the block id found there, the layer l
+// (pack only) and the side (unpack and the fused kernel take one side of a
+// block per work item). per = tiles per block-table entry (L for pack, else 1).
 struct TileAt {
     int32_t si;
     int32_t l;
+    int32_t side;
     int64_t b;
     int32_t blk;
 };
 
 template <class Batch>
-__device__ __forceinline__ TileAt tile_at(const Batch& batch, int32_t per, int64_t tile)
+__device__ __forceinline__ TileAt tile_at(const Batch& batch, int32_t per, int64_t tile,
+                                          int32_t side)
 {
     TileAt t;
     t.si = find_record(batch.tile0, batch.n, tile);
     const int64_t rem = tile - batch.tile0[t.si];
     t.b = per == 1 ? rem : rem / per;
     t.l = int32_t(rem - t.b * per);
+    t.side = side;
     t.blk = batch.rec[t.si].block_table[t.b];
     return t;
 }
 
-// Workgroup blockIdx.x takes tiles order[i] for i = blockIdx.x, + grid, ...
-// (a null order means tile i). Under a workgroup budget one workgroup copies
-// many tiles in turn, so the next tile's record and block id are fetched
-// before the current tile is copied, and the order entry one tile further
-// ahead: the dependent metadata loads then overlap a copy instead of sitting
-// between two. With one workgroup per tile the loop body runs once.
+// Work item i is side i % sides of tile order[i / sides] (a null order means
+// tile i / sides); workgroup blockIdx.x takes items blockIdx.x, + grid, ...
+// Under a workgroup budget one workgroup copies many items in turn, so the
+// next item's record and block id are fetched before the current item is
+// copied, and the order entry one item further ahead: the dependent metadata
+// loads then overlap a copy instead of sitting between two. With one
+// workgroup per item the loop body runs once.
 template <class Batch, class Body>
-__device__ __forceinline__ void walk_tiles(const Batch& batch, int32_t per,
+__device__ __forceinline__ void walk_tiles(const Batch& batch, int32_t per, int32_t sides,
                                            const int32_t* __restrict__ order, Body body)
 {
-    const int64_t n = batch.tile0[batch.n];
+    const int64_t n = batch.tile0[batch.n] * sides;
     const int64_t grid = gridDim.x;
+    auto tile_of = [&](int64_t i) {
+        const int64_t p = sides == 1 ? i : sides == 2 ? (i >> 1) : i / sides;
+        return order ? int64_t(order[p]) : p;
+    };
+    auto side_of = [&](int64_t i) {
+        return sides == 1 ? 0 : sides == 2 ? int32_t(i & 1) : int32_t(i % sides);
+    };
     int64_t i = blockIdx.x;
     if (i >= n) return;
-    TileAt cur = tile_at(batch, per, order ? int64_t(order[i]) : i);
-    int64_t next = i + grid < n ? (order ? int64_t(order[i + grid]) : i + grid) : 0;
+    TileAt cur = tile_at(batch, per, tile_of(i), side_of(i));
+    int64_t next = i + grid < n ? tile_of(i + grid) : 0;
     for (;;) {
         const bool more = i + grid < n;
         TileAt nxt = cur;
-        if (more) nxt = tile_at(batch, per, next);
+        if (more) nxt = tile_at(batch, per, next, side_of(i + grid));
         const int64_t j = i + 2 * grid;
-        const int64_t after = j < n ? (order ? int64_t(order[j]) : j) : 0;
+        const int64_t after = j < n ? tile_of(j) : 0;
         body(cur);
         if (!more) break;
         cur = nxt;
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
                                              FastDiv div_q, FastDiv div_v,
                                              unsigned long long* err)
 {
-    walk_tiles(batch, num_layers, nullptr, [&](const TileAt& t) {
+    walk_tiles(batch, num_layers, 1, nullptr, [&](const TileAt& t) {
         const SeqRec& s = batch.rec[t.si];
         const int64_t b = t.b;
         const int32_t l = t.l;
@@ -249,36 +262,36 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
 }
 
 // -------------------------------------------------------------- unpack ---
-// pool[layer][s][bt[t / B]][t % B] <- full[t][layer][s] for the tokens of one
-// block below num_tokens; same element order as k_pack. Workgroup i takes tile
-// order[i]: the tiles sorted by destination block id (k_order_*), so the
-// object stores of concurrently running workgroups ascend through the pool
-// instead of landing at random. A null order keeps the tiles' own order.
+// pool[layer][side][bt[t / B]][t % B] <- full[t][layer][side] for the tokens
+// of one block below num_tokens. A work item is one side of one block tile:
+// B strided row pieces read, one contiguous object written (measured on
+// MI355X: 3 % faster than one item per block with both sides). Element j of
+// an item is row j / V, unit column j % V. Items are taken in the tiles'
+// order[] (sorted by destination block id, k_order_*), so the object stores
+// of concurrently running workgroups ascend through the pool instead of
+// landing at random. A null order keeps the tiles' own order.
 template <int U, int BS, int UNR, bool WM>
 __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ pool, int32_t layer,
                                                const SeqBatch batch, const int32_t* __restrict__ order,
-                                               FastDiv div_q, FastDiv div_v,
-                                               unsigned long long* err)
+                                               FastDiv div_v, unsigned long long* err)
 {
-    walk_tiles(batch, 1, order, [&](const TileAt& t) {
+    walk_tiles(batch, 1, g.sides, order, [&](const TileAt& t) {
         const SeqRec& s = batch.rec[t.si];
-        const int64_t b = t.b;
         const int32_t blk = t.blk;
         if (bad_block(blk, g.num_blocks)) {
-            if (threadIdx.x == 0) atomicAdd(err, 1ull);
+            if (threadIdx.x == 0 && t.side == 0) atomicAdd(err, 1ull);
             return;
         }
-        const int64_t t0 = b * g.block_tokens;
+        const int64_t t0 = t.b * g.block_tokens;
         const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-        const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
-        char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
-        copy_elements<U, BS, UNR, WM>(rows * div_q.d, [&](uint32_t j, const char*& sp, char*& dp) {
-            const uint32_t r = fdiv(j, div_q);
-            const uint32_t q = j - r * div_q.d;
-            const uint32_t side = fdiv(q, div_v);
-            const uint32_t c = q - side * div_v.d;
-            sp = src + int64_t(r) * s.token_stride + int64_t(q) * U;
-            dp = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
+        const char* src = s.full + t0 * s.token_stride +
+                          (int64_t(layer) * g.sides + t.side) * g.row_bytes;
+        char* dst = pool + layer * g.layer_stride + t.side * g.side_stride + blk * g.block_stride;
+        copy_elements<U, BS, UNR, WM>(rows * div_v.d, [&](uint32_t j, const char*& sp, char*& dp) {
+            const uint32_t r = fdiv(j, div_v);
+            const uint32_t c = j - r * div_v.d;
+            sp = src + int64_t(r) * s.token_stride + int64_t(c) * U;
+            dp = dst + int64_t(r) * g.row_bytes + int64_t(c) * U;
         });
     });
 }
@@ -286,30 +299,30 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
 // ---------------------------------------------------- unpack + merge ---
 // The hit rows of one layer, read once and stored twice: into the block-table
 // slots (as k_unpack) and into the request's output rows t0..t0+rows (as the
-// hit part of k_merge). Same tiles, order and element order as k_unpack; the
-// second store of element j goes to out + (t0 + r)*out_stride + q*U.
+// hit part of k_merge). Same work items, order and element order as k_unpack;
+// the second store of element j (row r, column c) of side s goes to
+// out + (t0 + r)*out_stride + s*row_bytes + c*U.
 template <int U, int BS, int UNR, bool WM>
 __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restrict__ pool,
                                                      int32_t layer, const LayerBatch batch,
                                                      const int32_t* __restrict__ order,
-                                                     FastDiv div_q, FastDiv div_v,
-                                                     unsigned long long* err)
+                                                     FastDiv div_v, unsigned long long* err)
 {
     typedef typename Unit<U>::T V;
-    walk_tiles(batch, 1, order, [&](const TileAt& t) {
+    walk_tiles(batch, 1, g.sides, order, [&](const TileAt& t) {
         const LayerRec& s = batch.rec[t.si];
-        const int64_t b = t.b;
         const int32_t blk = t.blk;
         if (bad_block(blk, g.num_blocks)) {
-            if (threadIdx.x == 0) atomicAdd(err, 1ull);
+            if (threadIdx.x == 0 && t.side == 0) atomicAdd(err, 1ull);
             return;
         }
-        const int64_t t0 = b * g.block_tokens;
+        const int64_t t0 = t.b * g.block_tokens;
         const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-        const uint32_t total = rows * div_q.d;
-        const char* src = s.full + t0 * s.token_stride + int64_t(layer) * g.sides * g.row_bytes;
-        char* dst = pool + layer * g.layer_stride + blk * g.block_stride;
-        char* out = s.out + t0 * s.out_stride;
+        const uint32_t total = rows * div_v.d;
+        const char* src = s.full + t0 * s.token_stride +
+                          (int64_t(layer) * g.sides + t.side) * g.row_bytes;
+        char* dst = pool + layer * g.layer_stride + t.side * g.side_stride + blk * g.block_stride;
+        char* out = s.out + t0 * s.out_stride + int64_t(t.side) * g.row_bytes;
         constexpr uint32_t kStep = WM ? 64 : BS;
         const uint32_t first = WM ? (threadIdx.x >> 6) * (64 * UNR) + (threadIdx.x & 63) : threadIdx.x;
         const uint32_t limit = WM ? total + BS * UNR : total;
@@ -321,14 +334,12 @@ __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restric
             for (int k = 0; k < UNR; ++k) {
                 const uint32_t j = base + k * kStep;
                 if (j < total) {
-                    const uint32_t r = fdiv(j, div_q);
-                    const uint32_t q = j - r * div_q.d;
-                    const uint32_t side = fdiv(q, div_v);
-                    const uint32_t c = q - side * div_v.d;
+                    const uint32_t r = fdiv(j, div_v);
+                    const uint32_t c = j - r * div_v.d;
                     v[k] = ld(reinterpret_cast<const V*>(src + int64_t(r) * s.token_stride +
-                                                         int64_t(q) * U));
-                    dp[k] = dst + side * g.side_stride + int64_t(r) * g.row_bytes + int64_t(c) * U;
-                    op[k] = out + int64_t(r) * s.out_stride + int64_t(q) * U;
+                                                         int64_t(c) * U));
+                    dp[k] = dst + int64_t(r) * g.row_bytes + int64_t(c) * U;
+                    op[k] = out + int64_t(r) * s.out_stride + int64_t(c) * U;
                 }
             }
 #pragma unroll
@@ -606,7 +617,7 @@ __global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__
     default: CALL(1); break;                          \
     }
 
-// Grid of a tile kernel: one workgroup per tile, or the budget if smaller.
+// Grid of a tile kernel: one workgroup per work item, or the budget if smaller.
 static dim3 tile_grid(int64_t ntiles, int32_t max_wgs)
 {
     return dim3(uint32_t(max_wgs > 0 ? std::min<int64_t>(ntiles, max_wgs) : ntiles));
@@ -648,11 +659,10 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
                          unsigned long long* err, int32_t max_wgs, hipStream_t st)
 {
     (void)num_layers;
-    const uint32_t v = uint32_t(g.row_bytes / unit);
-    const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
-    const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
+    const FastDiv dv = make_fastdiv(uint32_t(g.row_bytes / unit));
+    const dim3 grid = tile_grid(b.tile0[b.n] * g.sides, max_wgs);
 #define KVM_UNPACK(U)                                                                       \
-    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dq, dv, err)
+    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_UNPACK)
 #undef KVM_UNPACK
     return hipGetLastError();
@@ -662,12 +672,11 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
                                const LayerBatch& b, const int32_t* order,
                                unsigned long long* err, int32_t max_wgs, hipStream_t st)
 {
-    const uint32_t v = uint32_t(g.row_bytes / unit);
-    const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
-    const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
+    const FastDiv dv = make_fastdiv(uint32_t(g.row_bytes / unit));
+    const dim3 grid = tile_grid(b.tile0[b.n] * g.sides, max_wgs);
 #define KVM_FUSED(U)                                                                        \
     hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, kFusedWaveMajor>), grid,   \
-                       dim3(kFusedBS), 0, st, g, pool, layer, b, order, dq, dv, err)
+                       dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_FUSED)
 #undef KVM_FUSED
     return hipGetLastError();
