@@ -40,7 +40,8 @@ def budget_ctx(ctx, request):
     (5, 2, 500, 3, 48, [2, 1] * 70, "dense"),        # 140 sequences: two launches
     (3, 1, 300, 64, 1152, [700, 65, 0], "slot"),
     (2, 2, 30, 4, 5, [23, 9], "block_major"),         # byte moves
-], ids=["dense", "many-seqs", "mla-slot", "bytes"])
+    (3, 3, 50, 8, 64, [40, 9], "block_major"),        # three sides
+], ids=["dense", "many-seqs", "mla-slot", "bytes", "three-sides"])
 def test_budget_pack_unpack(budget_ctx, gpu, case):
     L, S, N, B, rb, Ts, kind = case
     run_pack_unpack(budget_ctx, gpu, L, S, N, B, rb, Ts, kind=kind,
@@ -64,7 +65,8 @@ def test_budget_merge(budget_ctx, gpu, case):
     # (L, S, N, B, rb, reqs, kind)
     (3, 2, 200, 16, 512, [(300, 20), (0, 9), (13, 0), (0, 0), (64, 64)], "dense"),
     (2, 2, 700, 3, 48, [(5, 2), (1, 1)] * 70, "block_major"),
-], ids=["mixed", "many-reqs"])
+    (2, 3, 100, 4, 32, [(23, 5), (9, 0), (0, 3)], "dense"),     # three sides
+], ids=["mixed", "many-reqs", "three-sides"])
 def test_budget_unpack_merge(budget_ctx, gpu, case):
     L, S, N, B, rb, reqs, kind = case
     run_unpack_merge(budget_ctx, gpu, L, S, N, B, rb, reqs, kind=kind,

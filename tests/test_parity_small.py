@@ -81,6 +81,8 @@ PACK_CASES = [
     (2, 2, 64, 16, 256, [100, 50], "dense", 0, 0, 1),                    # odd base address
     (1, 1, 8, 7, 16, [0, 0, 5], "slot", 0, 0, 0),
     (2, 2, 70000, 1, 16, [10, 3], "dense", 0, 0, 0),                    # pool >> tiles: own order
+    (2, 3, 40, 4, 48, [33, 7], "dense", 0, 0, 0),                       # three sides
+    (3, 5, 30, 2, 32, [19, 4, 1], "block_major", 0, 16, 0),             # five sides, padded tokens
 ]
 
 
@@ -290,6 +292,8 @@ FUSED_CASES = [
     (2, 2, 700, 3, 48, [(5, 2), (1, 1)] * 70, "block_major", 0, 0, 0, 0),   # 140 requests
     (2, 2, 60, 4, 12, [(23, 5), (9, 0)], "dense", 4, 4, 4, 4),               # 4-byte moves
     (2, 2, 60, 4, 5, [(23, 5), (9, 2)], "dense", 3, 1, 5, 1),                # byte moves
+    (2, 3, 60, 4, 32, [(23, 5), (9, 0), (0, 3)], "dense", 0, 0, 16, 0),     # three sides
+    (3, 5, 40, 2, 16, [(13, 2), (6, 1)], "slot", 16, 0, 0, 0),              # five sides
 ]
 
 
