@@ -111,6 +111,15 @@ def test_llama8b_layer_loop(ctx, gpu, fused):
             oracle.pack_full(got_slab, slot, 1, tables[r], t_all, exp)
             assert np.array_equal(layer_slice(packed[r], t_all, L, C, l), exp), \
                 f"pack_full layer {l} request {r}"
+    # Every layer and request, by a property of the three operations: a hit token's
+    # row in the packed Full Block (read back from its slot after unpack) equals
+    # its row in complete_layer (merged from the same hit slice).
+    say("  checking pack_full == complete_layer on the hit rows of every layer")
+    for r in range(R):
+        pk = packed[r].view(t_all, L, C)
+        cm = complete[r * L * t_all * C:(r + 1) * L * t_all * C].view(L, t_all, C)
+        for l in range(L):
+            assert torch.equal(pk[:t_hit, l], cm[l, :t_hit]), f"layer {l} request {r}"
     del pool, fbs, misses, complete, packed
     torch.cuda.empty_cache()
 
@@ -212,6 +221,20 @@ def test_mla_agentic_layer_loop(ctx, gpu, fused):
             kv.kvm_merge_layer(ctx.handle, C, [
                 kv.merge_seq(fbs[r].data_ptr() + l * C, L * C, w.t_hit[r], mbase + int(moff[r]),
                              C, w.t_miss[r], out.data_ptr() + int(roff[r]), C) for r in range(R)])
+        # Every layer and request, by the operations' defining properties (on the
+        # device, after the moves on the same stream): complete_layer is the layer's
+        # hit slice then its miss rows, and hit token t sits in slot (bt[t / B], t % B).
+        slots = slot.view(N, B, C)
+        for r in range(R):
+            th = w.t_hit[r]
+            fbl = fbs[r].view(th, L, C)[:, l]
+            o = out[int(roff[r]):int(roff[r + 1])].view(-1, C)
+            mr = misses[l * int(moff[-1]) + int(moff[r]):l * int(moff[-1]) + int(moff[r + 1])]
+            assert torch.equal(o[:th], fbl), f"complete_layer hit rows, layer {l} request {r}"
+            assert torch.equal(o[th:], mr.view(-1, C)), f"complete_layer miss rows, layer {l}"
+            t = torch.arange(th, device=gpu)
+            assert torch.equal(slots[bts[r].long()[t // B], t % B], fbl), \
+                f"slot rows, layer {l} request {r}"
         if pre is None:
             continue
         torch.cuda.synchronize()
