@@ -124,6 +124,37 @@ def test_llama8b_layer_loop(ctx, gpu, fused):
     torch.cuda.empty_cache()
 
 
+def _check_all_objects(src, dst, descs, granule=256, batch=2048):
+    """Every object, on the device: dst[dst_off, +n) == src[src_off, +n). All
+    offsets are multiples of `granule`, so each length class is compared through
+    strided windows of the two buffers."""
+    descs_t = torch.from_numpy(descs.astype(np.int64)).to(src.device)
+    for n in np.unique(descs[:, 2]):
+        n = int(n)
+        sel = descs_t[descs_t[:, 2] == n]
+        ws = src.unfold(0, n, granule)
+        wd = dst.unfold(0, n, granule)
+        for a in range(0, len(sel), batch):
+            part = sel[a:a + batch]
+            assert torch.equal(wd[part[:, 1] // granule], ws[part[:, 0] // granule]), \
+                f"an object of {n} bytes differs"
+
+
+def _check_untouched(dst, descs, granule=256, chunk=1 << 22):
+    """Every granule of dst that no object covers still holds the sentinel."""
+    covered = torch.zeros(dst.numel() // granule, dtype=torch.bool, device=dst.device)
+    d = torch.from_numpy(descs.astype(np.int64)).to(dst.device)
+    first, count = d[:, 1] // granule, d[:, 2] // granule
+    idx = torch.repeat_interleave(first, count) + (
+        torch.arange(int(count.sum().item()), device=dst.device)
+        - torch.repeat_interleave(torch.cumsum(count, 0) - count, count))
+    covered[idx] = True
+    g = dst.view(-1, granule)
+    for a in range(0, g.shape[0], chunk):
+        free = ~covered[a:a + chunk]
+        assert bool((g[a:a + chunk][free] == SENTINEL).all().item()), "a byte outside every object was written"
+
+
 def _check_copies(src, dst, descs, sample, gaps=None):
     for k in sample:
         so, do, n = (int(x) for x in descs[k])
@@ -162,6 +193,7 @@ def test_qwen32b_object_restore(ctx, gpu):
         say(f"  checking {mode}")
         assert ctx.take_device_errors() == 0
         _check_copies(staging, pool, descs_np, sample)
+        _check_all_objects(staging, pool, descs_np)
         # the objects tile the pool exactly: the first 64 bytes of every object
         # were overwritten (64 random bytes all equal to the sentinel: p = 2^-512)
         heads = pool.view(-1, 131072)[:, :64]
@@ -280,5 +312,8 @@ def test_small_objects(ctx, gpu):
     gaps = [(int(ends[i]), int(starts[i + 1])) for i in rng.choice(n - 1, 300, replace=False)
             if starts[i + 1] > ends[i]]
     _check_copies(src, dst, descs_np, sample, gaps)
+    say("  checking every object and every uncovered granule")
+    _check_all_objects(src, dst, descs_np)
+    _check_untouched(dst, descs_np)
     del src, dst, descs
     torch.cuda.empty_cache()
