@@ -212,18 +212,21 @@ __device__ __forceinline__ void copy_elements(uint32_t total, Addr addr)
 // variants timed in one process on the same buffers, interleaved): pack and
 // merge keep a whole 64 KiB tile in flight per workgroup, pack in wave-major
 // order (+2.4 % over thread-major), merge in thread-major order (wave-major
-// costs it 18 %). Unpack, whose stores land on scattered pool objects, and
-// the fused kernel take 576 threads x 8 units (72 KiB in flight, one 64-row
-// MLA tile of 1152-byte rows exactly): against 256 x 8 that moves 1-1.6 %
-// more on the Llama layer loop and 3 % more on the MLA loop, where 512 x 8
-// gains only on MLA. No occupancy cap helps unpack.
+// costs it 18 %). Unpack, whose stores land on scattered pool objects, takes
+// 576 threads x 8 units for items of up to 2048 units (the 32 KiB side of a
+// Llama block: 5.83 TB/s, against 5.56 at 256 x 8 and 5.58 at 1024 x 8) and
+// 1024 x 8 for larger items (a 72 KiB MLA block: 6.11 TB/s against 5.53 at
+// 576 x 8). The fused kernel takes 1024 x 8 for every size (+2 % on Llama,
+// +7 % on MLA against 576 x 8). No occupancy cap helps either.
 constexpr int kPackBS = 1024, kPackUnroll = 4;
 constexpr bool kPackWaveMajor = true;
 constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
 constexpr int kUnpackBS = 576, kUnpackUnroll = 8;
 constexpr bool kUnpackWaveMajor = false;
-constexpr int kFusedBS = 576, kFusedUnroll = 8;
+constexpr int kUnpackWideBS = 1024, kUnpackWideUnroll = 8;
+constexpr int64_t kUnpackWideItem = 2048;   // 16-byte units per item above which
+constexpr int kFusedBS = 1024, kFusedUnroll = 8;
 constexpr bool kFusedWaveMajor = false;
 
 // ---------------------------------------------------------------- pack ---
@@ -661,6 +664,11 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
     (void)num_layers;
     const FastDiv dv = make_fastdiv(uint32_t(g.row_bytes / unit));
     const dim3 grid = tile_grid(b.tile0[b.n] * g.sides, max_wgs);
+    if (unit == 16 && int64_t(g.block_tokens) * (g.row_bytes / 16) > kUnpackWideItem) {
+        hipLaunchKernelGGL((k_unpack<16, kUnpackWideBS, kUnpackWideUnroll, kUnpackWaveMajor>), grid,
+                           dim3(kUnpackWideBS), 0, st, g, pool, layer, b, order, dv, err);
+        return hipGetLastError();
+    }
 #define KVM_UNPACK(U)                                                                       \
     hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_UNPACK)
