@@ -1,0 +1,61 @@
+"""include/kvm.h is a plain C header: a C11 program that includes it compiles
+with warnings as errors, links against libkvmove.so and calls the entry points
+that need no device (version, status text, argument checks)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from paged_kv_cache_kvm_amd import kvmove
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+PROGRAM = r"""
+#include "kvm.h"
+#include <stdio.h>
+#include <string.h>
+
+int main(void)
+{
+    kvm_ctx* ctx = NULL;
+    kvm_pool_layout layout;
+    kvm_seq seq;
+    kvm_merge_seq mseq;
+    kvm_layer_seq lseq;
+    kvm_copy_desc desc;
+    memset(&layout, 0, sizeof layout);
+    memset(&seq, 0, sizeof seq);
+    memset(&mseq, 0, sizeof mseq);
+    memset(&lseq, 0, sizeof lseq);
+    memset(&desc, 0, sizeof desc);
+    if (kvm_version() != KVM_ABI_VERSION) return 1;
+    if (strcmp(kvm_strerror(KVM_EINVAL), "invalid argument") != 0) return 2;
+    if (kvm_create(0, NULL) != KVM_EINVAL) return 3;
+    if (kvm_create(-1, &ctx) != KVM_EINVAL) return 4;
+    if (kvm_pack_full(NULL, &layout, NULL, 1, &seq, 1, NULL) != KVM_EINVAL) return 5;
+    if (kvm_unpack_layer(NULL, &layout, NULL, 1, 0, &seq, 1, NULL) != KVM_EINVAL) return 6;
+    if (kvm_merge_layer(NULL, 16, &mseq, 1, NULL) != KVM_EINVAL) return 7;
+    if (kvm_unpack_merge_layer(NULL, &layout, NULL, 1, 0, &lseq, 1, NULL) != KVM_EINVAL) return 8;
+    if (kvm_batch_copy(NULL, NULL, 0, NULL, 0, &desc, 1, NULL) != KVM_EINVAL) return 9;
+    if (kvm_ctx_set_max_workgroups(NULL, 1) != KVM_EINVAL) return 10;
+    kvm_destroy(NULL);
+    printf("%d %d %d %d %d\n", (int)sizeof(kvm_pool_layout), (int)sizeof(kvm_seq),
+           (int)sizeof(kvm_merge_seq), (int)sizeof(kvm_layer_seq), (int)sizeof(kvm_copy_desc));
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+def test_header_compiles_as_c11_and_links(tmp_path):
+    src = tmp_path / "abi.c"
+    src.write_text(PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(kvmove.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", libdir, "-lkvmove", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    assert out.stdout.split() == ["48", "32", "64", "72", "24"]
