@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PCIE_PEAK_GBS = 63.0   # PCIe 5.0 x16 host link, per direction
 
 
 def log(msg):
@@ -190,8 +191,10 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
     """The pages' host-DRAM prompt buffers: request 0's Full Block in pinned host
     memory. Per layer: unpack_layer reads its hit slice over PCIe into the HBM
     pool (Prefill side); merge_layer writes complete_layer into a pinned host
-    buffer (Decode side, hit rows from HBM). Rates are PCIe bytes per second,
-    next to torch's pinned host<->device copy rates."""
+    buffer (Decode side, hit rows from HBM); pack_full writes the request's whole
+    Full Block (all T_all tokens) into pinned host memory (persisting it). Rates
+    are PCIe bytes per second, next to torch's pinned host<->device copy rates
+    and the PCIe 5.0 x16 peak (63 GB/s per direction)."""
     L, C = s["L"], s["C"]
     bts, fbs, misses, _, _ = s["keep"]
     t_hit, t_miss = 32768, 512
@@ -199,6 +202,7 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
     host_fb = torch.empty(fbs[0].numel(), dtype=torch.uint8, pin_memory=True)
     host_fb.copy_(fbs[0])
     host_out = torch.empty(t_all * C, dtype=torch.uint8, pin_memory=True)
+    host_packed = torch.empty(t_all * L * C, dtype=torch.uint8, pin_memory=True)
     dev_buf = torch.empty(1 << 30, dtype=torch.uint8, device=fbs[0].device)
     host_buf = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
     seqs = [kv.seq(bts[0], host_fb, t_hit)]
@@ -214,11 +218,16 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
                 fbs[0].data_ptr() + l * C, L * C, t_hit, misses[0].data_ptr() + l * C, L * C,
                 t_miss, host_out, C)])
 
+    def pack_host():
+        kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, [kv.seq(bts[0], host_packed, t_all)])
+
     unpack_loop()
     merge_loop()
+    pack_host()
     for _ in range(reps):
         ev.around("h2d_unpack", unpack_loop)
         ev.around("d2h_merge", merge_loop)
+        ev.around("d2h_pack", pack_host)
         ev.around("h2d_copy", lambda: dev_buf.copy_(host_buf, non_blocking=True))
         ev.around("d2h_copy", lambda: host_buf.copy_(dev_buf, non_blocking=True))
     torch.cuda.synchronize()
@@ -226,17 +235,26 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
     mg_gbs = L * t_all * C / (ev.mean_ms("d2h_merge") * 1e6)
     h2d = (1 << 30) / (ev.mean_ms("h2d_copy") * 1e6)
     d2h = (1 << 30) / (ev.mean_ms("d2h_copy") * 1e6)
-    del host_fb, host_out, dev_buf, host_buf
+    pk_gbs = t_all * L * C / (ev.mean_ms("d2h_pack") * 1e6)
+    del host_fb, host_out, host_packed, dev_buf, host_buf
     return {"workload": "request 0 of the layer loop, Full Block / complete_layer in pinned host memory",
             "unpack_layer_from_host": {"pcie_bytes_per_launch": t_hit * C,
                                        "ms_per_launch": round(ev.mean_ms("h2d_unpack") / L, 3),
                                        "pcie_GBps": round(up_gbs, 1),
-                                       "frac_of_h2d_copy": round(up_gbs / h2d, 3)},
+                                       "frac_of_h2d_copy": round(up_gbs / h2d, 3),
+                                       "frac_of_pcie_peak": round(up_gbs / PCIE_PEAK_GBS, 3)},
             "merge_layer_into_host": {"pcie_bytes_per_launch": t_all * C,
                                       "ms_per_launch": round(ev.mean_ms("d2h_merge") / L, 3),
                                       "pcie_GBps": round(mg_gbs, 1),
-                                      "frac_of_d2h_copy": round(mg_gbs / d2h, 3)},
-            "torch_pinned_copy_GBps": {"h2d": round(h2d, 1), "d2h": round(d2h, 1)}}
+                                      "frac_of_d2h_copy": round(mg_gbs / d2h, 3),
+                                      "frac_of_pcie_peak": round(mg_gbs / PCIE_PEAK_GBS, 3)},
+            "pack_full_into_host": {"pcie_bytes_per_launch": t_all * L * C,
+                                    "ms_per_launch": round(ev.mean_ms("d2h_pack"), 3),
+                                    "pcie_GBps": round(pk_gbs, 1),
+                                    "frac_of_d2h_copy": round(pk_gbs / d2h, 3),
+                                    "frac_of_pcie_peak": round(pk_gbs / PCIE_PEAK_GBS, 3)},
+            "torch_pinned_copy_GBps": {"h2d": round(h2d, 1), "d2h": round(d2h, 1)},
+            "pcie_peak_GBps_per_direction": PCIE_PEAK_GBS}
 
 
 def pipeline_section(torch, kv, ctx, s, reps=3, d_model=4096, d_ff=14336):
