@@ -5,8 +5,8 @@
 // in flight per CU, keeping every lane busy on ragged rows, and never writing
 // a partial cache line that a full row would cover:
 //
-//   k_pack / k_unpack   one workgroup per work item. A pack item is
-//                       (sequence, block, layer); an unpack item is
+//   k_pack / k_unpack /  one workgroup per work item. A pack item is
+//   k_unpack_merge      (sequence, block, layer); an unpack or fused item is
 //                       (sequence, block, side).
 //                       With a workgroup budget below the item count, the
 //                       grid is the budget and workgroup i takes items i,
@@ -15,8 +15,9 @@
 //                       An item's rows are flattened into one index space of
 //                       `unit`-byte elements so that a 1152-byte MLA row or a
 //                       256-byte tiny row keeps every lane busy; element ->
-//                       (row, side, column) uses multiply-high division by
-//                       invariant integers.
+//                       (row, side, column) for pack, (row, column) for the
+//                       others, uses multiply-high division by invariant
+//                       integers.
 //   k_merge             a tile is (request, chunk of rows); a row comes from
 //                       the strided hit slice or from the miss rows. The grid
 //                       is capped (16 workgroups per CU), and each workgroup
@@ -225,7 +226,8 @@ constexpr bool kMergeWaveMajor = false;
 constexpr int kUnpackBS = 576, kUnpackUnroll = 8;
 constexpr bool kUnpackWaveMajor = false;
 constexpr int kUnpackWideBS = 1024, kUnpackWideUnroll = 8;
-constexpr int64_t kUnpackWideItem = 2048;   // 16-byte units per item above which
+constexpr int64_t kUnpackWideItem = 2048;  // 16-byte units per item above which unpack
+                                           // takes the wide shape
 constexpr int kFusedBS = 1024, kFusedUnroll = 8;
 constexpr bool kFusedWaveMajor = false;
 

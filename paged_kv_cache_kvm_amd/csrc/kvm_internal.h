@@ -99,13 +99,14 @@ struct CopyDesc {
 // All launches go to `st` and return the launch status. `unit` is the move
 // width in bytes (16, 8, 4, 2 or 1) that divides every address and stride.
 // max_wgs > 0 caps the grid of a tile kernel (each workgroup then loops over
-// tiles i, i + grid, ...); 0 launches one workgroup per tile.
+// work items i, i + grid, ...); 0 launches one workgroup per work item.
 hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
                        const SeqBatch& b, unsigned long long* err, int32_t max_wgs,
                        hipStream_t st);
 
-// order: a permutation of the batch's tiles (workgroup i takes tile order[i]),
-// made by launch_unpack_order; null keeps the tiles' own order.
+// One work item per (tile, side): item i is side i % sides of tile
+// order[i / sides]. order: a permutation of the batch's tiles made by
+// launch_unpack_order; null keeps the tiles' own order.
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
                          int32_t layer, const SeqBatch& b, const int32_t* order,
                          unsigned long long* err, int32_t max_wgs, hipStream_t st);
