@@ -57,10 +57,12 @@
  *     object outside its buffer is skipped (its destination is left as it was)
  *     and counted; kvm_take_device_errors() returns the count.
  *   - One context per host thread; calls on one context are not thread-safe.
- *   - Preconditions the library does not check: the block tables of one call
+ *   - Caller preconditions: the block tables of one unpack or fused call
  *     hold no repeated entry; pool rows described by the layout do not overlap;
  *     copy destinations are pairwise disjoint and do not overlap the sources.
- *     Violations give an unspecified (but in-bounds) result.
+ *     Violations give an unspecified (but in-bounds) result. The kernels do
+ *     not check them; kvm_ctx_set_checks turns on host-side checks of the
+ *     first and the last (a debug mode).
  */
 #ifndef KVM_H
 #define KVM_H
@@ -79,6 +81,8 @@ extern "C" {
 #define KVM_ERANGE (-2) /* layer outside [0, L), a size above a supported limit   */
 #define KVM_ENOMEM (-3) /* device or pinned host memory could not be obtained      */
 #define KVM_EHIP (-4)   /* a HIP runtime call or launch failed; see kvm_ctx_last_error */
+#define KVM_ECHECK (-5) /* checks on (kvm_ctx_set_checks): a caller precondition is
+                           violated; see kvm_ctx_last_error */
 
 typedef struct kvm_ctx kvm_ctx;
 
@@ -192,7 +196,24 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
  * KVM_EINVAL (null ctx, max_workgroups < 0). */
 int kvm_ctx_set_max_workgroups(kvm_ctx* ctx, int32_t max_workgroups);
 
-/* Text of the last HIP failure seen by this context ("" if none). */
+/* Debug mode: with enable != 0, every later unpack, fused and batched-copy
+ * call first checks on the host the caller preconditions the kernels cannot
+ * see, and returns KVM_ECHECK, with the offending entries named in
+ * kvm_ctx_last_error, having enqueued nothing:
+ *   kvm_unpack_layer, kvm_unpack_merge_layer: no valid block id appears
+ *     twice among the block-table entries the call writes (all sequences);
+ *   kvm_batch_copy: destination ranges are pairwise disjoint, and disjoint
+ *     from every source range when the two buffers overlap.
+ * Entries the kernels skip anyway (ids outside [0, num_blocks), objects
+ * outside their buffer, zero-length objects) are not violations. A checked
+ * call synchronises `stream` and copies the block tables or the descriptor
+ * array to the host: it is for debugging, not the hot path. New contexts
+ * start with checks on when the environment variable KVM_CHECK is "1".
+ * Errors: KVM_EINVAL (null ctx). */
+int kvm_ctx_set_checks(kvm_ctx* ctx, int32_t enable);
+
+/* Text of the last HIP failure or check violation seen by this context ("" if
+ * none). */
 const char* kvm_ctx_last_error(const kvm_ctx* ctx);
 
 /* Synchronise the context's device, then return in *count the number of

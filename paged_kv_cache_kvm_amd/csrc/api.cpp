@@ -6,8 +6,10 @@
 #include "kvm_internal.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 using kvm::CopyDesc;
@@ -56,6 +58,7 @@ struct kvm_ctx {
     int device = 0;
     int num_cus = 0;
     int32_t max_wgs = 0;           // workgroup budget of every move launch; 0 = none
+    bool checks = false;           // host-side precondition checks before each call
     unsigned long long* d_err = nullptr;
     uint64_t* d_groups = nullptr;  // group sums, then group bases
     int64_t group_cap = 0;         // groups the scratch holds
@@ -313,6 +316,97 @@ int grow_groups(kvm_ctx* c, int64_t groups)
     return KVM_OK;
 }
 
+// ------------------------------------------------ precondition checks ---
+// Debug mode (kvm_ctx_set_checks): the preconditions the kernels cannot see
+// are verified on the host before anything is enqueued. The caller's stream is
+// synchronised first, since the tables or descriptors may be written by work
+// already on it.
+
+int fail_check(kvm_ctx* ctx, const std::string& what)
+{
+    ctx->last_error = "precondition: " + what;
+    return KVM_ECHECK;
+}
+
+// No valid block id appears twice among the given tables (n entries each).
+// Ids outside [0, num_blocks) are not a precondition violation: the kernels
+// skip and count them.
+int check_unique_blocks(kvm_ctx* ctx, hipStream_t st,
+                        const std::vector<std::pair<const int32_t*, int64_t>>& tables,
+                        int64_t num_blocks)
+{
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_hip(ctx, e, "hipStreamSynchronize");
+    std::vector<int32_t> ids;
+    for (const auto& t : tables) {
+        const size_t at = ids.size();
+        ids.resize(at + size_t(t.second));
+        e = hipMemcpy(ids.data() + at, t.first, size_t(t.second) * sizeof(int32_t),
+                      hipMemcpyDefault);
+        if (e != hipSuccess) return fail_hip(ctx, e, "hipMemcpy (block table check)");
+    }
+    ids.erase(std::remove_if(ids.begin(), ids.end(),
+                             [&](int32_t v) { return v < 0 || int64_t(v) >= num_blocks; }),
+              ids.end());
+    std::sort(ids.begin(), ids.end());
+    const auto dup = std::adjacent_find(ids.begin(), ids.end());
+    if (dup != ids.end())
+        return fail_check(ctx, "block id " + std::to_string(*dup) +
+                                   " is written twice by one call (repeated block-table entry)");
+    return KVM_OK;
+}
+
+// Copy destinations are pairwise disjoint, and disjoint from every source
+// range when the two buffers overlap. Objects outside their buffer are not a
+// violation (the kernels skip and count them) and are left out.
+int check_copy_list(kvm_ctx* ctx, hipStream_t st, uintptr_t dst_base, uint64_t dst_bytes,
+                    uintptr_t src_base, uint64_t src_bytes, const kvm_copy_desc* descs,
+                    int64_t n)
+{
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail_hip(ctx, e, "hipStreamSynchronize");
+    std::vector<kvm_copy_desc> h(static_cast<size_t>(n));
+    e = hipMemcpy(h.data(), descs, size_t(n) * sizeof(kvm_copy_desc), hipMemcpyDefault);
+    if (e != hipSuccess) return fail_hip(ctx, e, "hipMemcpy (copy list check)");
+    struct Range { uint64_t a, b; int64_t k; };  // absolute [a, b), descriptor index
+    std::vector<Range> dst, src;
+    for (int64_t k = 0; k < n; ++k) {
+        const kvm_copy_desc& x = h[size_t(k)];
+        if (x.nbytes == 0) continue;
+        const bool ok = x.src_off <= src_bytes && x.nbytes <= src_bytes - x.src_off &&
+                        x.dst_off <= dst_bytes && x.nbytes <= dst_bytes - x.dst_off;
+        if (!ok) continue;
+        dst.push_back({dst_base + x.dst_off, dst_base + x.dst_off + x.nbytes, k});
+        src.push_back({src_base + x.src_off, src_base + x.src_off + x.nbytes, k});
+    }
+    auto by_start = [](const Range& p, const Range& q) { return p.a < q.a; };
+    std::sort(dst.begin(), dst.end(), by_start);
+    for (size_t i = 1; i < dst.size(); ++i)
+        if (dst[i].a < dst[i - 1].b)
+            return fail_check(ctx, "copy objects " + std::to_string(dst[i - 1].k) + " and " +
+                                       std::to_string(dst[i].k) + " overlap in the destination");
+    const bool buffers_overlap = dst_base < src_base + src_bytes && src_base < dst_base + dst_bytes;
+    if (!buffers_overlap || dst.empty()) return KVM_OK;
+    // merge the source ranges, then look each destination range up among them
+    std::sort(src.begin(), src.end(), by_start);
+    std::vector<Range> merged;
+    for (const Range& r : src) {
+        if (!merged.empty() && r.a <= merged.back().b) merged.back().b = std::max(merged.back().b, r.b);
+        else merged.push_back(r);
+    }
+    for (const Range& d : dst) {
+        auto it = std::upper_bound(merged.begin(), merged.end(), d.a,
+                                   [](uint64_t v, const Range& r) { return v < r.a; });
+        if (it != merged.end() && it->a < d.b)
+            return fail_check(ctx, "copy object " + std::to_string(d.k) +
+                                       " writes over a source range");
+        if (it != merged.begin() && std::prev(it)->b > d.a)
+            return fail_check(ctx, "copy object " + std::to_string(d.k) +
+                                       " writes over a source range");
+    }
+    return KVM_OK;
+}
+
 // merge_layer records split into launch batches, with the widest move unit
 // that divides every pointer and stride seen.
 struct MergePlan {
@@ -381,6 +475,7 @@ const char* kvm_strerror(int status)
     case KVM_ERANGE: return "argument out of range";
     case KVM_ENOMEM: return "out of memory";
     case KVM_EHIP: return "HIP runtime error";
+    case KVM_ECHECK: return "precondition violated (checks on)";
     default: return "unknown status";
     }
 }
@@ -395,6 +490,8 @@ int kvm_create(int device, kvm_ctx** out)
     kvm_ctx* c = new (std::nothrow) kvm_ctx();
     if (!c) return KVM_ENOMEM;
     c->device = device;
+    const char* env = std::getenv("KVM_CHECK");
+    c->checks = env && std::strcmp(env, "1") == 0;
     if (hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, device) !=
             hipSuccess ||
         c->num_cus <= 0) {
@@ -444,6 +541,13 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs)
     return grow_groups(ctx, (max_descs + kvm::kDescGroup - 1) / kvm::kDescGroup);
 }
 
+int kvm_ctx_set_checks(kvm_ctx* ctx, int32_t enable)
+{
+    if (!ctx) return KVM_EINVAL;
+    ctx->checks = enable != 0;
+    return KVM_OK;
+}
+
 int kvm_ctx_set_max_workgroups(kvm_ctx* ctx, int32_t max_workgroups)
 {
     if (!ctx || max_workgroups < 0) return KVM_EINVAL;
@@ -490,6 +594,14 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ctx->checks && !pack) {
+        std::vector<std::pair<const int32_t*, int64_t>> tables;
+        for (const kvm::SeqBatch& b : plan.batches)
+            for (int32_t i = 0; i < b.n; ++i)
+                tables.emplace_back(b.rec[i].block_table, b.tile0[i + 1] - b.tile0[i]);
+        rc = check_unique_blocks(ctx, st, tables, layout->num_blocks);
+        if (rc != KVM_OK) return rc;
+    }
     const PoolGeom g = geom_of(layout);
     std::vector<OrderSlot*> orders(plan.batches.size(), nullptr);
     if (!pack) {
@@ -618,6 +730,14 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ctx->checks) {
+        std::vector<std::pair<const int32_t*, int64_t>> tables;
+        for (const kvm::SeqBatch& b : keys)
+            for (int32_t i = 0; i < b.n; ++i)
+                tables.emplace_back(b.rec[i].block_table, b.tile0[i + 1] - b.tile0[i]);
+        rc = check_unique_blocks(ctx, st, tables, layout->num_blocks);
+        if (rc != KVM_OK) return rc;
+    }
     std::vector<OrderSlot*> orders(hit.size(), nullptr);
     for (size_t i = 0; i < hit.size(); ++i) {
         if (layout->num_blocks > 16 * hit[i].tile0[hit[i].n] + 65536) continue;
@@ -644,6 +764,12 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     if (n_descs > kMaxDescs) return KVM_ERANGE;
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
+    if (ctx->checks) {
+        const int rc = check_copy_list(ctx, static_cast<hipStream_t>(stream),
+                                       uintptr_t(dst_base), dst_bytes, uintptr_t(src_base),
+                                       src_bytes, descs, n_descs);
+        if (rc != KVM_OK) return rc;
+    }
     const int64_t groups = (n_descs + kvm::kDescGroup - 1) / kvm::kDescGroup;
     int rc = grow_groups(ctx, groups);
     if (rc != KVM_OK) return rc;

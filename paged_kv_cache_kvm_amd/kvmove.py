@@ -17,7 +17,7 @@ from typing import Iterable, Sequence
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvmove.so")
 
-KVM_OK, KVM_EINVAL, KVM_ERANGE, KVM_ENOMEM, KVM_EHIP = 0, -1, -2, -3, -4
+KVM_OK, KVM_EINVAL, KVM_ERANGE, KVM_ENOMEM, KVM_EHIP, KVM_ECHECK = 0, -1, -2, -3, -4, -5
 
 
 class KvmError(RuntimeError):
@@ -70,6 +70,7 @@ SIGNATURES = {
     "kvm_create": ([ctypes.c_int, ctypes.POINTER(_P)], ctypes.c_int),
     "kvm_destroy": ([_P], None),
     "kvm_ctx_reserve": ([_P, _I64, _I64], ctypes.c_int),
+    "kvm_ctx_set_checks": ([_P, _I32], ctypes.c_int),
     "kvm_ctx_set_max_workgroups": ([_P, _I32], ctypes.c_int),
     "kvm_ctx_last_error": ([_P], ctypes.c_char_p),
     "kvm_take_device_errors": ([_P, ctypes.POINTER(_I64)], ctypes.c_int),
@@ -125,7 +126,7 @@ def _stream(s) -> int | None:
 def _check(fn: str, status: int, ctx=None):
     if status != KVM_OK:
         detail = ""
-        if ctx is not None and status == KVM_EHIP:
+        if ctx is not None and status in (KVM_EHIP, KVM_ECHECK):
             detail = (load().kvm_ctx_last_error(ctx) or b"").decode()
         raise KvmError(fn, status, detail)
 
@@ -153,6 +154,10 @@ def kvm_destroy(ctx: int) -> None:
 
 def kvm_ctx_reserve(ctx: int, max_seqs: int, max_descs: int) -> None:
     _check("kvm_ctx_reserve", load().kvm_ctx_reserve(ctx, max_seqs, max_descs), ctx)
+
+
+def kvm_ctx_set_checks(ctx: int, enable: bool) -> None:
+    _check("kvm_ctx_set_checks", load().kvm_ctx_set_checks(ctx, 1 if enable else 0), ctx)
 
 
 def kvm_ctx_set_max_workgroups(ctx: int, max_workgroups: int) -> None:
@@ -260,6 +265,9 @@ class Context:
 
     def reserve(self, max_seqs: int, max_descs: int):
         kvm_ctx_reserve(self.handle, max_seqs, max_descs)
+
+    def set_checks(self, enable: bool):
+        kvm_ctx_set_checks(self.handle, enable)
 
     def set_max_workgroups(self, max_workgroups: int):
         kvm_ctx_set_max_workgroups(self.handle, max_workgroups)

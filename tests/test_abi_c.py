@@ -39,6 +39,8 @@ int main(void)
     if (kvm_unpack_merge_layer(NULL, &layout, NULL, 1, 0, &lseq, 1, NULL) != KVM_EINVAL) return 8;
     if (kvm_batch_copy(NULL, NULL, 0, NULL, 0, &desc, 1, NULL) != KVM_EINVAL) return 9;
     if (kvm_ctx_set_max_workgroups(NULL, 1) != KVM_EINVAL) return 10;
+    if (kvm_ctx_set_checks(NULL, 1) != KVM_EINVAL) return 11;
+    if (strcmp(kvm_strerror(KVM_ECHECK), "unknown status") == 0) return 12;
     kvm_destroy(NULL);
     printf("%d %d %d %d %d\n", (int)sizeof(kvm_pool_layout), (int)sizeof(kvm_seq),
            (int)sizeof(kvm_merge_seq), (int)sizeof(kvm_layer_seq), (int)sizeof(kvm_copy_desc));

@@ -39,7 +39,7 @@ def test_binding_covers_every_declared_symbol():
 def test_version_and_status_text():
     m = re.search(r"#define KVM_ABI_VERSION (\d+)", open(HEADER).read())
     assert kvmove.kvm_version() == int(m.group(1))
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert kvmove.strerror(code)
     assert kvmove.strerror(12345) == "unknown status"
 
@@ -47,7 +47,7 @@ def test_version_and_status_text():
 def test_status_codes_match_header():
     text = open(HEADER).read()
     for name, val in [("KVM_OK", 0), ("KVM_EINVAL", -1), ("KVM_ERANGE", -2), ("KVM_ENOMEM", -3),
-                      ("KVM_EHIP", -4)]:
+                      ("KVM_EHIP", -4), ("KVM_ECHECK", -5)]:
         assert re.search(rf"#define {name} \(?{re.escape(str(val))}\)?", text), name
         assert getattr(kvmove, name) == val
 
@@ -71,6 +71,7 @@ def test_null_arguments_rejected_without_a_device():
     assert lib.kvm_ctx_reserve(None, 1, 1) == kvmove.KVM_EINVAL
     assert lib.kvm_unpack_merge_layer(None, None, None, 1, 0, None, 0, None) == kvmove.KVM_EINVAL
     assert lib.kvm_ctx_set_max_workgroups(None, 4) == kvmove.KVM_EINVAL
+    assert lib.kvm_ctx_set_checks(None, 1) == kvmove.KVM_EINVAL
     lib.kvm_destroy(None)
 
 
