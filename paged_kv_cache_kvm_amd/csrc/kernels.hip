@@ -223,6 +223,7 @@ constexpr int kPackBS = 1024, kPackUnroll = 4;
 constexpr bool kPackWaveMajor = true;
 constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
+constexpr int kMergeWideUnroll = 8;  // short rows: 128 KiB tiles, 1024 x 8 in flight
 constexpr int kUnpackBS = 576, kUnpackUnroll = 8;
 constexpr bool kUnpackWaveMajor = false;
 constexpr int kUnpackWideBS = 1024, kUnpackWideUnroll = 8;
@@ -693,10 +694,15 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
 }
 
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
-                        int32_t max_wgs, hipStream_t st)
+                        bool wide, int32_t max_wgs, hipStream_t st)
 {
     const FastDiv dv = make_fastdiv(uint32_t(row_bytes / unit));
     const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
+    if (wide && unit == 16) {
+        hipLaunchKernelGGL((k_merge<16, kMergeBS, kMergeWideUnroll, kMergeWaveMajor>), grid,
+                           dim3(kMergeBS), 0, st, rows_per_tile, b, dv);
+        return hipGetLastError();
+    }
 #define KVM_MERGE(U)                                                                        \
     hipLaunchKernelGGL((k_merge<U, kMergeBS, kMergeUnroll, kMergeWaveMajor>), grid, dim3(kMergeBS), 0, st, rows_per_tile, b, dv)
     KVM_UNIT_SWITCH(unit, KVM_MERGE)

@@ -122,8 +122,10 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
 hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* count_scratch,
                                int32_t* order, hipStream_t st);
 
+// wide: 16-byte moves keep 1024 x 8 units in flight per workgroup (for tiles
+// of 128 KiB) instead of 1024 x 4.
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
-                        int32_t max_wgs, hipStream_t st);
+                        bool wide, int32_t max_wgs, hipStream_t st);
 
 // group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1. copy_blocks
 // workgroups are launched; when the objects average 64 KiB or more and total
