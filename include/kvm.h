@@ -188,12 +188,11 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
  * Prefill; Tutti reading notes, design 2: I/O kernels kept to a few SMs
  * beside compute). The bytes written are the same for every budget.
  * 0 (the default) keeps the library's own grids: one workgroup per work item
- * for pack, unpack and the fused call, at most 16 workgroups per CU for merge and
- * 8 per CU for the batched copy. The destination-order sort
- * that unpack runs once per new set of block tables is not bounded (it
- * touches 8 bytes per tile). Applies to calls enqueued
- * after it returns; calls already enqueued keep their grids. Errors:
- * KVM_EINVAL (null ctx, max_workgroups < 0). */
+ * for pack, unpack and the fused call, at most 16 workgroups per CU for merge
+ * and 8 per CU for the batched copy. The destination-order sort that unpack
+ * runs once per new set of block tables is not bounded (it touches 8 bytes
+ * per tile). Applies to calls enqueued after it returns; calls already
+ * enqueued keep their grids. Errors: KVM_EINVAL (null ctx, max_workgroups < 0). */
 int kvm_ctx_set_max_workgroups(kvm_ctx* ctx, int32_t max_workgroups);
 
 /* Debug mode: with enable != 0, every later unpack, fused and batched-copy
@@ -217,8 +216,9 @@ int kvm_ctx_set_checks(kvm_ctx* ctx, int32_t enable);
 const char* kvm_ctx_last_error(const kvm_ctx* ctx);
 
 /* Synchronise the context's device, then return in *count the number of
- * tiles (a block-table entry, per layer for pack) and copy objects that
- * device-side guards skipped since the previous call, and reset the counter. Errors: KVM_EINVAL, KVM_EHIP. */
+ * block-table entries (counted once per layer for pack) and copy objects that
+ * device-side guards skipped since the previous call, and reset the counter.
+ * Errors: KVM_EINVAL, KVM_EHIP. */
 int kvm_take_device_errors(kvm_ctx* ctx, int64_t* count);
 
 /* Pack (DualPath key-objects table, the persisted Full Block): for each
@@ -246,7 +246,8 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  * stream (a counting sort over the pool's blocks, kept in the context for the
  * following layers; skipped when the pool has far more blocks than the call
  * has tiles). Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
- * [0, num_layers) or more than 2048 sequences with tokens in one call. */
+ * [0, num_layers) or more than 2048 sequences with tokens in one call, and
+ * KVM_ECHECK (checks on, kvm_ctx_set_checks). */
 int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
                      int32_t num_layers, int32_t layer, const kvm_seq* seqs, int32_t n,
                      void* stream);
@@ -290,7 +291,8 @@ typedef struct {
  * read once: 3*H + 2*M bytes move instead of 4*H + 2*M. Launches: one fused
  * kernel per 128 requests for the hit rows (tiles in destination-block order,
  * as kvm_unpack_layer) and one for the miss rows.
- * Errors: the union of kvm_unpack_layer's and kvm_merge_layer's. */
+ * Errors: the union of kvm_unpack_layer's and kvm_merge_layer's (KVM_ECHECK
+ * included). */
 int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
                            int32_t num_layers, int32_t layer, const kvm_layer_seq* seqs,
                            int32_t n, void* stream);
@@ -305,9 +307,10 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
  * counted (kvm_take_device_errors). Zero-length objects are no-ops. The bytes
  * are split evenly over the device's wavefronts (8 workgroups per CU, or 2
  * when the objects average 64 KiB or more and the call moves 1 GiB or more),
- * so a few large objects and many small ones balance alike. dst_base and src_base may be the same
- * buffer. Errors: KVM_EINVAL (null ctx, null descs/bases with n_descs > 0,
- * n_descs < 0), KVM_ERANGE (n_descs above 2^32), KVM_ENOMEM, KVM_EHIP. */
+ * so a few large objects and many small ones balance alike. dst_base and
+ * src_base may be the same buffer. Errors: KVM_EINVAL (null ctx, null
+ * descs/bases with n_descs > 0, n_descs < 0), KVM_ERANGE (n_descs above 2^32),
+ * KVM_ENOMEM, KVM_EHIP, KVM_ECHECK (checks on). */
 int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,
                    uint64_t src_bytes, const kvm_copy_desc* descs, int64_t n_descs,
                    void* stream);
