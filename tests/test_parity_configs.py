@@ -317,3 +317,27 @@ def test_small_objects(ctx, gpu):
     _check_untouched(dst, descs_np)
     del src, dst, descs
     torch.cuda.empty_cache()
+
+
+def test_one_object_above_4gib(ctx, gpu):
+    """One 5 GiB + 5 byte object at offsets 3 and 19 (equal modulo 16: a byte
+    head, 16-byte body, byte tail), so lengths and vector counts need 64 bits.
+    Every byte is compared on the device; the bytes around it keep the sentinel."""
+    n = (5 << 30) + 5
+    size = n + 64
+    need_free(2 * size + (1 << 30))
+    say(f"  one object of {n} bytes")
+    u8 = dict(dtype=torch.uint8, device=gpu)
+    src = torch.empty(size, **u8)
+    wl.fill_random_bytes_(src, 1006, 1)
+    dst = torch.full((size,), SENTINEL, **u8)
+    descs_np = np.array([[3, 19, n]], np.uint64)
+    descs = torch.from_numpy(descs_np.view(np.uint8).reshape(-1)).to(gpu)
+    kv.kvm_batch_copy(ctx.handle, dst, size, src, size, descs, 1)
+    torch.cuda.synchronize()
+    assert ctx.take_device_errors() == 0
+    assert torch.equal(dst[19:19 + n], src[3:3 + n])
+    assert bool((dst[:19] == SENTINEL).all().item())
+    assert bool((dst[19 + n:] == SENTINEL).all().item())
+    del src, dst, descs
+    torch.cuda.empty_cache()
