@@ -97,6 +97,37 @@ def test_unpack_sequence_limit(ctx, bufs):
     assert np.all(down(pool) == SENTINEL)
 
 
+def test_size_limits_are_refused(ctx, bufs):
+    """The documented maximum sizes: 2^31 work items in one launch (tiles x
+    sides for unpack, tiles x layers for pack), a tile of 2^31 bytes or more,
+    more than 2^20 sequences, and more than 2^32 copy objects. Each is refused
+    before anything is read from the (here too small) buffers."""
+    pool, bt, full = bufs
+    lay1 = kv.pool_layout(S, 1, RB, RB, N * RB, S * N * RB, N)        # B = 1
+    huge = [kv.seq(bt, full, 1 << 31)]                               # 2^31 tiles
+    half = [kv.seq(bt, full, (1 << 30) + 1)]                          # x 2 sides > 2^31
+    cases = [
+        ((kv.kvm_unpack_layer, ctx.handle, lay1, pool, L, 0, huge), kv.KVM_ERANGE),
+        ((kv.kvm_unpack_layer, ctx.handle, lay1, pool, L, 0, half), kv.KVM_ERANGE),
+        ((kv.kvm_pack_full, ctx.handle, lay1, pool, L, [kv.seq(bt, full, 1 << 30)]), kv.KVM_ERANGE),
+        ((kv.kvm_unpack_merge_layer, ctx.handle, lay1, pool, L, 0,
+          [kv.layer_seq(bt, full, (1 << 30) + 1, 0, 0, 0, pool, S * RB)]), kv.KVM_ERANGE),
+        ((kv.kvm_unpack_layer, ctx.handle,
+          kv.pool_layout(S, 1 << 16, 1 << 15, 1 << 31, 1 << 32, 1 << 33, N), pool, L, 0,
+          [kv.seq(bt, full, 1)]), kv.KVM_ERANGE),                     # 2^32-byte tile
+    ]
+    for args, want in cases:
+        assert _status(*args) == want, args[0].__name__
+    lib = kv.load()
+    one = (kv.kvm_seq * 1)(kv.seq(bt, full, 1))
+    assert lib.kvm_unpack_layer(ctx.handle, ctypes.byref(_layout()), pool.data_ptr(), L, 0, one,
+                                (1 << 20) + 1, None) == kv.KVM_ERANGE
+    assert lib.kvm_batch_copy(ctx.handle, pool.data_ptr(), 64, full.data_ptr(), 64, bt.data_ptr(),
+                              (1 << 32) + 1, None) == kv.KVM_ERANGE
+    torch.cuda.synchronize()
+    assert np.all(down(pool) == SENTINEL), "a refused call wrote"
+
+
 def test_degenerate_calls_are_noops(ctx, bufs):
     pool, bt, full = bufs
     lay = _layout()
