@@ -302,3 +302,61 @@ def test_unpack_merge(ctx, gpu, case):
     L, S, N, B, rb, reqs, kind, tp, mp, op, off = case
     run_unpack_merge(ctx, gpu, L, S, N, B, rb, reqs, kind=kind, ts_pad=tp, miss_pad=mp,
                      out_pad=op, offset=off, seed=hash(str(case)) & 0xFFFF)
+
+
+def test_one_context_on_two_streams(gpu):
+    """One context used on two streams with no host synchronisation between
+    calls: the destination order sorted on stream A is reused by stream B (which
+    must wait for the sort), and batched copies alternate streams over the
+    shared group scratch (each must wait for the previous call's kernels)."""
+    say("  two streams, one context")
+    c = kv.Context(0)
+    try:
+        L, S, N, B, rb = 4, 2, 300, 16, 256
+        layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+        ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+        rng = np.random.default_rng(61)
+        Ts = [700, 333, 1201]
+        tables = wl.block_tables(61, 1, N, [wl.blocks_needed(t, B) for t in Ts])
+        fb_np = [rng.integers(0, 256, T * L * S * rb, dtype=np.uint8) for T in Ts]
+        want = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
+        for layer in range(L):
+            for i, T in enumerate(Ts):
+                oracle.unpack_layer(want, ref, L, layer, tables[i], T, fb_np[i])
+        bts = [up(t, gpu) for t in tables]
+        fbs = [up(f, gpu) for f in fb_np]
+        pool = up(np.full(L * S * N * B * rb, SENTINEL, np.uint8), gpu)
+        seqs = [kv.seq(bts[i], fbs[i], T) for i, T in enumerate(Ts)]
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        for layer in range(L):            # the sort runs on a; layers alternate a, b
+            kv.kvm_unpack_layer(c.handle, layout, pool, L, layer, seqs, stream=a if layer % 2 == 0 else b)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(pool), want)
+
+        # batched copies alternating streams
+        src_np = rng.integers(0, 256, 1 << 22, dtype=np.uint8)
+        src = up(src_np, gpu)
+        dst = up(np.full(1 << 22, SENTINEL, np.uint8), gpu)
+        lists, dlists = [], []
+        region = (1 << 22) // 6                  # list k writes only its own region of dst
+        region -= region % 256
+        for k in range(6):
+            lens = 256 * rng.integers(1, 16, size=200)
+            d = np.stack([wl.placements(70 + k, 1, lens, 1 << 22),
+                          k * region + wl.placements(70 + k, 2, lens, region), lens],
+                         axis=1).astype(np.uint64)
+            lists.append(d)
+            dlists.append(up(d.view(np.uint8), gpu))
+        want_dst = np.full(1 << 22, SENTINEL, np.uint8)
+        for d in lists:
+            oracle.batch_copy(want_dst, src_np, d)
+        torch.cuda.synchronize()
+        for k, d in enumerate(dlists):     # no waits between the calls: the library's own
+            kv.kvm_batch_copy(c.handle, dst, 1 << 22, src, 1 << 22, d, len(lists[k]),
+                              stream=a if k % 2 == 0 else b)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(dst), want_dst)
+        assert c.take_device_errors() == 0
+    finally:
+        c.close()
