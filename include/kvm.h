@@ -179,6 +179,25 @@ void kvm_destroy(kvm_ctx* ctx);
  * KVM_EHIP. */
 int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
 
+/* Pre-size the unpack tile-order scratch: every order slot of the context
+ * (16) holds max_tiles entries, and the counting sort serves pools of up to
+ * max_pool_blocks blocks. Later kvm_unpack_layer and kvm_unpack_merge_layer
+ * calls whose launch batches (128 sequences each) hold at most max_tiles
+ * block-table entries, on pools of at most max_pool_blocks blocks, allocate
+ * no device memory. With kvm_ctx_reserve for the batched copy this gives an
+ * allocation-free steady state. Synchronises the device and drops cached
+ * orders that it resizes. Uses 64 * max_tiles + 8 * max_pool_blocks bytes
+ * (plus a small constant). Errors: KVM_EINVAL (null ctx, negative sizes),
+ * KVM_ERANGE (max_tiles above 2^31 - 1, max_pool_blocks above 2^31),
+ * KVM_ENOMEM, KVM_EHIP. */
+int kvm_ctx_reserve_unpack(kvm_ctx* ctx, int64_t max_tiles, int64_t max_pool_blocks);
+
+/* Device memory the context holds right now, in bytes: its error counter,
+ * the batched-copy scratch and the unpack order scratch. It changes only
+ * when a call (or a reserve) grows or frees that scratch. Errors: KVM_EINVAL
+ * (null ctx or bytes). */
+int kvm_ctx_device_bytes(const kvm_ctx* ctx, int64_t* bytes);
+
 /* Workgroup budget: every later pack, unpack, merge, fused and batched-copy
  * launch through this context uses a grid of at most max_workgroups
  * workgroups, each of which loops over the tiles (or byte shares) that a

@@ -63,6 +63,7 @@ struct kvm_ctx {
     int num_cus = 0;
     int32_t max_wgs = 0;           // workgroup budget of every move launch; 0 = none
     bool checks = false;           // host-side precondition checks before each call
+    int64_t device_bytes = 0;      // device memory held by this context
     unsigned long long* d_err = nullptr;
     uint64_t* d_groups = nullptr;  // group sums, then group bases
     int64_t group_cap = 0;         // groups the scratch holds
@@ -106,6 +107,28 @@ int fail_hip(kvm_ctx* ctx, hipError_t e, const char* what)
 {
     if (ctx) ctx->last_error = std::string(what) + ": " + hipGetErrorString(e);
     return KVM_EHIP;
+}
+
+// Every device allocation of a context goes through these two, so that
+// kvm_ctx_device_bytes can report what the context holds.
+template <class T>
+bool dev_alloc(kvm_ctx* c, T** p, size_t count)
+{
+    if (hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T)) != hipSuccess) {
+        *p = nullptr;
+        return false;
+    }
+    c->device_bytes += int64_t(count * sizeof(T));
+    return true;
+}
+
+template <class T>
+void dev_free(kvm_ctx* c, T*& p, size_t count)
+{
+    if (!p) return;
+    (void)hipFree(p);
+    c->device_bytes -= int64_t(count * sizeof(T));
+    p = nullptr;
 }
 
 // Widest move unit (16, 8, 4, 2, 1 bytes) that divides every value OR-ed in.
@@ -194,14 +217,13 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
 void order_release(kvm_ctx* c)
 {
     for (OrderSlot& o : c->orders) {
-        if (o.order) (void)hipFree(o.order);
+        dev_free(c, o.order, size_t(o.cap));
         if (o.ready) (void)hipEventDestroy(o.ready);
         if (o.last_use) (void)hipEventDestroy(o.last_use);
         o = OrderSlot();
     }
-    if (c->d_count) (void)hipFree(c->d_count);
+    dev_free(c, c->d_count, size_t(c->count_cap));
     if (c->count_done) (void)hipEventDestroy(c->count_done);
-    c->d_count = nullptr;
     c->count_cap = 0;
     c->count_done = nullptr;
 }
@@ -251,12 +273,9 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
             return fail_hip(c, e, "hipEventCreateWithFlags");
     }
     if (o->cap < ntiles) {
-        if (o->order) (void)hipFree(o->order);
-        o->order = nullptr;
+        dev_free(c, o->order, size_t(o->cap));
         o->cap = 0;
-        if (hipMalloc(reinterpret_cast<void**>(&o->order), size_t(ntiles) * sizeof(int32_t)) !=
-            hipSuccess) {
-            o->order = nullptr;
+        if (!dev_alloc(c, &o->order, size_t(ntiles))) {
             c->last_error = "hipMalloc: unpack order";
             return KVM_ENOMEM;
         }
@@ -266,13 +285,10 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     if (c->count_cap < words) {
         e = hipDeviceSynchronize();
         if (e != hipSuccess) return fail_hip(c, e, "hipDeviceSynchronize");
-        if (c->d_count) (void)hipFree(c->d_count);
-        c->d_count = nullptr;
+        dev_free(c, c->d_count, size_t(c->count_cap));
         c->count_cap = 0;
         c->count_pending = false;
-        if (hipMalloc(reinterpret_cast<void**>(&c->d_count), size_t(words) * sizeof(uint32_t)) !=
-            hipSuccess) {
-            c->d_count = nullptr;
+        if (!dev_alloc(c, &c->d_count, size_t(words))) {
             c->last_error = "hipMalloc: unpack order scratch";
             return KVM_ENOMEM;
         }
@@ -306,14 +322,11 @@ int grow_groups(kvm_ctx* c, int64_t groups)
     if (groups <= c->group_cap) return KVM_OK;
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail_hip(c, e, "hipDeviceSynchronize");
-    if (c->d_groups) (void)hipFree(c->d_groups);
-    c->d_groups = nullptr;
+    if (c->d_groups) dev_free(c, c->d_groups, size_t(2 * c->group_cap + 1));
     c->group_cap = 0;
     const int64_t cap = std::max<int64_t>(groups, 1024);
-    e = hipMalloc(reinterpret_cast<void**>(&c->d_groups), size_t(2 * cap + 1) * sizeof(uint64_t));
-    if (e != hipSuccess) {
-        c->d_groups = nullptr;
-        c->last_error = std::string("hipMalloc: ") + hipGetErrorString(e);
+    if (!dev_alloc(c, &c->d_groups, size_t(2 * cap + 1))) {
+        c->last_error = "hipMalloc: batched-copy group scratch";
         return KVM_ENOMEM;
     }
     c->group_cap = cap;
@@ -504,12 +517,12 @@ int kvm_create(int device, kvm_ctx** out)
         delete c;
         return KVM_EHIP;
     }
-    if (hipMalloc(reinterpret_cast<void**>(&c->d_err), sizeof(unsigned long long)) != hipSuccess) {
+    if (!dev_alloc(c, &c->d_err, 1)) {
         delete c;
         return KVM_ENOMEM;
     }
     if (hipMemset(c->d_err, 0, sizeof(unsigned long long)) != hipSuccess) {
-        (void)hipFree(c->d_err);
+        dev_free(c, c->d_err, 1);
         delete c;
         return KVM_EHIP;
     }
@@ -533,8 +546,8 @@ void kvm_destroy(kvm_ctx* ctx)
     (void)hipDeviceSynchronize();
     order_release(ctx);
     if (ctx->copy_done) (void)hipEventDestroy(ctx->copy_done);
-    if (ctx->d_groups) (void)hipFree(ctx->d_groups);
-    if (ctx->d_err) (void)hipFree(ctx->d_err);
+    if (ctx->d_groups) dev_free(ctx, ctx->d_groups, size_t(2 * ctx->group_cap + 1));
+    dev_free(ctx, ctx->d_err, 1);
     delete ctx;
 }
 
@@ -545,6 +558,57 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs)
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
     return grow_groups(ctx, (max_descs + kvm::kDescGroup - 1) / kvm::kDescGroup);
+}
+
+int kvm_ctx_reserve_unpack(kvm_ctx* ctx, int64_t max_tiles, int64_t max_pool_blocks)
+{
+    if (!ctx || max_tiles < 0 || max_pool_blocks < 0) return KVM_EINVAL;
+    if (max_tiles > kMaxTiles || max_pool_blocks > (int64_t(1) << 31)) return KVM_ERANGE;
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return KVM_EHIP;
+    hipError_t e = hipDeviceSynchronize();  // no order or count array may be in use
+    if (e != hipSuccess) return fail_hip(ctx, e, "hipDeviceSynchronize");
+    for (OrderSlot& o : ctx->orders) {
+        if (!o.ready) {
+            if ((e = hipEventCreateWithFlags(&o.ready, hipEventDisableTiming)) != hipSuccess ||
+                (e = hipEventCreateWithFlags(&o.last_use, hipEventDisableTiming)) != hipSuccess)
+                return fail_hip(ctx, e, "hipEventCreateWithFlags");
+        }
+        if (o.cap < max_tiles) {
+            dev_free(ctx, o.order, size_t(o.cap));
+            o.cap = 0;
+            o.valid = false;
+            if (!dev_alloc(ctx, &o.order, size_t(max_tiles))) {
+                ctx->last_error = "hipMalloc: unpack order";
+                return KVM_ENOMEM;
+            }
+            o.cap = max_tiles;
+        }
+    }
+    const int64_t words = 2 * (max_pool_blocks + 2);
+    if (ctx->count_cap < words) {
+        dev_free(ctx, ctx->d_count, size_t(ctx->count_cap));
+        ctx->count_cap = 0;
+        ctx->count_pending = false;
+        if (!dev_alloc(ctx, &ctx->d_count, size_t(words))) {
+            ctx->last_error = "hipMalloc: unpack order scratch";
+            return KVM_ENOMEM;
+        }
+        ctx->count_cap = words;
+    }
+    if (!ctx->count_done &&
+        (e = hipEventCreateWithFlags(&ctx->count_done, hipEventDisableTiming)) != hipSuccess) {
+        ctx->count_done = nullptr;
+        return fail_hip(ctx, e, "hipEventCreateWithFlags");
+    }
+    return KVM_OK;
+}
+
+int kvm_ctx_device_bytes(const kvm_ctx* ctx, int64_t* bytes)
+{
+    if (!ctx || !bytes) return KVM_EINVAL;
+    *bytes = ctx->device_bytes;
+    return KVM_OK;
 }
 
 int kvm_ctx_set_checks(kvm_ctx* ctx, int32_t enable)

@@ -70,6 +70,8 @@ SIGNATURES = {
     "kvm_create": ([ctypes.c_int, ctypes.POINTER(_P)], ctypes.c_int),
     "kvm_destroy": ([_P], None),
     "kvm_ctx_reserve": ([_P, _I64, _I64], ctypes.c_int),
+    "kvm_ctx_reserve_unpack": ([_P, _I64, _I64], ctypes.c_int),
+    "kvm_ctx_device_bytes": ([_P, ctypes.POINTER(_I64)], ctypes.c_int),
     "kvm_ctx_set_checks": ([_P, _I32], ctypes.c_int),
     "kvm_ctx_set_max_workgroups": ([_P, _I32], ctypes.c_int),
     "kvm_ctx_last_error": ([_P], ctypes.c_char_p),
@@ -154,6 +156,17 @@ def kvm_destroy(ctx: int) -> None:
 
 def kvm_ctx_reserve(ctx: int, max_seqs: int, max_descs: int) -> None:
     _check("kvm_ctx_reserve", load().kvm_ctx_reserve(ctx, max_seqs, max_descs), ctx)
+
+
+def kvm_ctx_reserve_unpack(ctx: int, max_tiles: int, max_pool_blocks: int) -> None:
+    _check("kvm_ctx_reserve_unpack", load().kvm_ctx_reserve_unpack(ctx, max_tiles, max_pool_blocks),
+           ctx)
+
+
+def kvm_ctx_device_bytes(ctx: int) -> int:
+    n = _I64()
+    _check("kvm_ctx_device_bytes", load().kvm_ctx_device_bytes(ctx, ctypes.byref(n)), ctx)
+    return n.value
 
 
 def kvm_ctx_set_checks(ctx: int, enable: bool) -> None:
@@ -265,6 +278,12 @@ class Context:
 
     def reserve(self, max_seqs: int, max_descs: int):
         kvm_ctx_reserve(self.handle, max_seqs, max_descs)
+
+    def reserve_unpack(self, max_tiles: int, max_pool_blocks: int):
+        kvm_ctx_reserve_unpack(self.handle, max_tiles, max_pool_blocks)
+
+    def device_bytes(self) -> int:
+        return kvm_ctx_device_bytes(self.handle)
 
     def set_checks(self, enable: bool):
         kvm_ctx_set_checks(self.handle, enable)

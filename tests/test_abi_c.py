@@ -40,6 +40,11 @@ int main(void)
     if (kvm_batch_copy(NULL, NULL, 0, NULL, 0, &desc, 1, NULL) != KVM_EINVAL) return 9;
     if (kvm_ctx_set_max_workgroups(NULL, 1) != KVM_EINVAL) return 10;
     if (kvm_ctx_set_checks(NULL, 1) != KVM_EINVAL) return 11;
+    if (kvm_ctx_reserve_unpack(NULL, 1, 1) != KVM_EINVAL) return 13;
+    {
+        int64_t bytes = 0;
+        if (kvm_ctx_device_bytes(NULL, &bytes) != KVM_EINVAL) return 14;
+    }
     if (strcmp(kvm_strerror(KVM_ECHECK), "unknown status") == 0) return 12;
     kvm_destroy(NULL);
     printf("%d %d %d %d %d\n", (int)sizeof(kvm_pool_layout), (int)sizeof(kvm_seq),

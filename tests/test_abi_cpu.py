@@ -72,6 +72,8 @@ def test_null_arguments_rejected_without_a_device():
     assert lib.kvm_unpack_merge_layer(None, None, None, 1, 0, None, 0, None) == kvmove.KVM_EINVAL
     assert lib.kvm_ctx_set_max_workgroups(None, 4) == kvmove.KVM_EINVAL
     assert lib.kvm_ctx_set_checks(None, 1) == kvmove.KVM_EINVAL
+    assert lib.kvm_ctx_reserve_unpack(None, 1, 1) == kvmove.KVM_EINVAL
+    assert lib.kvm_ctx_device_bytes(None, ctypes.byref(ctypes.c_int64())) == kvmove.KVM_EINVAL
     lib.kvm_destroy(None)
 
 
