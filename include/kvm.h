@@ -57,6 +57,11 @@
  *     object outside its buffer is skipped (its destination is left as it was)
  *     and counted; kvm_take_device_errors() returns the count.
  *   - One context per host thread; calls on one context are not thread-safe.
+ *     One context may be used on several streams: calls wait (on the device)
+ *     for the context's own scratch where two streams share it.
+ *   - HIP graph capture of these calls is not supported: a captured unpack or
+ *     fused launch refers to the context's cached tile order, which a later
+ *     call with other block tables may overwrite before the graph replays.
  *   - Caller preconditions: the block tables of one unpack or fused call
  *     hold no repeated entry; pool rows described by the layout do not overlap;
  *     copy destinations are pairwise disjoint and do not overlap the sources.
