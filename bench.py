@@ -15,12 +15,12 @@ Full Block / complete_layer over PCIe), the layerwise overlap of the moves
 with a stand-in compute stream under workgroup budgets, two device copy
 ceilings, the MLA agentic layer loop (61 layers, 576-element latent, 64
 requests), the small-object batched copy (200000 objects of 256*U{16..512}
-bytes), the 256,000-object restore list, and the oracle timed on the host
-cores on one request of the same workload.
+bytes), the 256,000-object restore list, the per-call cost of small calls,
+and the oracle timed on the host cores on one request of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-batch-copy]
                       [--no-host] [--no-pipeline] [--no-mla]
-                      [--no-restore]
+                      [--no-restore] [--no-small]
 """
 from __future__ import annotations
 
@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-mla", action="store_true", help="skip the MLA agentic layer loop")
     ap.add_argument("--no-restore", action="store_true",
                     help="skip the 256,000-object restore list")
+    ap.add_argument("--no-small", action="store_true", help="skip the small-call section")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the layerwise overlap section (workgroup-bounded moves)")
     return ap.parse_args()
@@ -500,6 +501,48 @@ def mla_section(torch, kv, wl, ctx, dev, reps=3):
     return out
 
 
+def small_call_section(torch, kv, wl, ctx, dev, calls=2000):
+    """Per-call cost of small calls, back to back on one stream with no sync in
+    between: the pages' case for batching is the submission cost per object.
+    unpack_layer of the tiny workload (one request of 240 hit tokens, 30 KiB),
+    a batched copy of 64 objects of 4 KiB, and for reference one torch device
+    copy of 4 KiB per call. Microseconds per call on the host clock, pipelined."""
+    w = wl.TINY
+    sh = w.shape
+    L, S, B, rb, N = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, w.pool_blocks
+    u8 = dict(dtype=torch.uint8, device=dev)
+    pool = torch.empty(L * S * N * B * rb, **u8)
+    t_hit = w.t_hit[0]
+    bt = torch.from_numpy(wl.block_tables(w.seed, 2, N, [wl.blocks_needed(t_hit, B)])[0]).to(dev)
+    full = torch.empty(t_hit * L * S * rb, **u8)
+    layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+    seqs = [kv.seq(bt, full, t_hit)]
+    import numpy as np
+    lens = np.full(64, 4096, np.int64)
+    d = np.stack([wl.placements(9, 1, lens, 1 << 22), wl.placements(9, 2, lens, 1 << 22), lens],
+                 axis=1).astype(np.uint64)
+    descs = torch.from_numpy(d.view(np.uint8).reshape(-1)).to(dev)
+    src, dst = torch.empty(1 << 22, **u8), torch.empty(1 << 22, **u8)
+    a, b = torch.empty(4096, **u8), torch.empty(4096, **u8)
+
+    def per_call(fn):
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / calls
+
+    return {"unpack_layer_tiny_us": round(per_call(
+                lambda: kv.kvm_unpack_layer(ctx.handle, layout, pool, L, 1, seqs)), 2),
+            "batch_copy_64x4KiB_us": round(per_call(
+                lambda: kv.kvm_batch_copy(ctx.handle, dst, 1 << 22, src, 1 << 22, descs, 64)), 2),
+            "torch_copy_4KiB_us": round(per_call(lambda: b.copy_(a)), 2),
+            "calls": calls}
+
+
 def restore_section(torch, kv, wl, ctx, dev, reps=10):
     """The long-sequence restore list (one 128,000-token sequence of a
     Qwen3-32B-like model, L=64, B=64: 256,000 K/V objects of 128 KiB from
@@ -695,6 +738,7 @@ def main():
     bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
     restore = None if args.no_batch_copy or args.no_restore else \
         restore_section(torch, kv, wl, ctx, dev)
+    small = None if args.no_small else small_call_section(torch, kv, wl, ctx, dev)
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
 
@@ -724,6 +768,7 @@ def main():
         "mla_layer_loop": mla,
         "batch_copy": bc,
         "batch_copy_restore": restore,
+        "small_calls": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
