@@ -1,0 +1,84 @@
+"""GPU parity on a seeded random sweep of small shapes (every byte against the
+oracle): random layers, sides (1-4), block sizes, row sizes (any byte count,
+so every move width), pool layouts, block and token-stride padding, base
+offsets, request counts and token counts, including empty requests; random
+merge row sizes and paddings; random copy lists with zero-length objects and
+arbitrary alignment. The oracle runs first in every runner, so a case that
+does not fit its buffers fails on the CPU before any kernel runs."""
+import numpy as np
+import pytest
+
+from gpu_util import SENTINEL, run_batch_copy, run_merge, run_pack_unpack, run_unpack_merge, say
+from paged_kv_cache_kvm_amd import kvmove as kv
+from paged_kv_cache_kvm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+ROW_BYTES = [1, 2, 3, 5, 8, 12, 16, 24, 48, 64, 100, 256, 576, 1152, 2048]
+KINDS = ["dense", "block_major", "slot"]
+
+
+def _paged_case(i):
+    r = np.random.default_rng([2024, i])
+    L, S = int(r.integers(1, 6)), int(r.integers(1, 5))
+    B, rb = int(r.integers(1, 21)), int(r.choice(ROW_BYTES))
+    n = int(r.integers(1, 7))
+    Ts = [int(t) for t in r.integers(0, 200, size=n)]
+    N = sum(wl.blocks_needed(t, B) for t in Ts) + int(r.integers(1, 20))
+    kind = KINDS[int(r.integers(0, 3))]
+    block_pad = int(r.choice([0, 0, 0, 3, 8, 16]))
+    ts_pad = int(r.choice([0, 0, 5, 16]))
+    offset = int(r.choice([0, 0, 1, 4, 8]))
+    return L, S, N, B, rb, Ts, kind, block_pad, ts_pad, offset
+
+
+@pytest.fixture(scope="module")
+def ctx(gpu):
+    c = kv.Context(0)
+    yield c
+    c.close()
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_pack_unpack(ctx, gpu, i):
+    L, S, N, B, rb, Ts, kind, bp, tp, off = _paged_case(i)
+    run_pack_unpack(ctx, gpu, L, S, N, B, rb, Ts, kind=kind, block_pad=bp, ts_pad=tp, offset=off,
+                    seed=3000 + i)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_unpack_merge(ctx, gpu, i):
+    L, S, N, B, rb, Ts, kind, _, tp, off = _paged_case(100 + i)
+    r = np.random.default_rng([2025, i])
+    reqs = [(t, int(r.integers(0, 60))) for t in Ts]
+    N = sum(wl.blocks_needed(h + m, B) for h, m in reqs) + 1
+    run_unpack_merge(ctx, gpu, L, S, N, B, rb, reqs, kind=kind, ts_pad=tp,
+                     miss_pad=int(r.choice([0, 0, 7, 16])), out_pad=int(r.choice([0, 0, 3, 32])),
+                     offset=off, seed=4000 + i)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_merge(ctx, gpu, i):
+    r = np.random.default_rng([2026, i])
+    C = int(r.choice([1, 3, 16, 36, 100, 512, 1152, 4096, 5000]))
+    reqs = [(int(r.integers(0, 300)), int(r.integers(0, 100))) for _ in range(int(r.integers(1, 9)))]
+    run_merge(ctx, gpu, C, reqs, L=int(r.integers(1, 7)), hit_pad=int(r.choice([0, 0, 3, 16])),
+              miss_pad=int(r.choice([0, 0, 5, 16])), out_pad=int(r.choice([0, 0, 1, 32])),
+              offset=int(r.choice([0, 0, 1, 8])), seed=5000 + i)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_batch_copy(ctx, gpu, i):
+    r = np.random.default_rng([2027, i])
+    n = int(r.integers(1, 3000))
+    lens = r.integers(0, 20000, size=n)
+    lens[r.random(n) < 0.05] = 0
+    dst_size = int(lens.sum()) + int(r.integers(0, 1 << 16)) + 1
+    src_size = int(r.integers(20000, 1 << 22))
+    dst_off = wl.placements(6000 + i, 1, lens, dst_size, granule=1)
+    src_off = r.integers(0, src_size - lens + 1)
+    descs = np.stack([src_off.astype(np.uint64), dst_off.astype(np.uint64),
+                      lens.astype(np.uint64)], axis=1)
+    say(f"  random copy case {i}")
+    run_batch_copy(ctx, gpu, r.integers(0, 256, src_size, dtype=np.uint8),
+                   np.full(dst_size, SENTINEL, np.uint8), descs, label=f"random {i}")
