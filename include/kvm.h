@@ -212,8 +212,11 @@ int kvm_ctx_device_bytes(const kvm_ctx* ctx, int64_t* bytes);
  * Prefill; Tutti reading notes, design 2: I/O kernels kept to a few SMs
  * beside compute). The bytes written are the same for every budget.
  * 0 (the default) keeps the library's own grids: one workgroup per work item
- * for pack, unpack and the fused call, at most 16 workgroups per CU for merge
- * and 8 per CU for the batched copy. The destination-order sort that unpack
+ * for pack, unpack and the fused call, and for merge of rows under 2 KiB
+ * (up to 4,194,303 workgroups, the most a dispatch of 1024-thread
+ * workgroups can count; above that each takes several items); at most 16
+ * workgroups per CU for merge of longer rows, and 8 per CU for the batched
+ * copy. The destination-order sort that unpack
  * runs once per new set of block tables is not bounded (it touches 8 bytes
  * per tile). Applies to calls enqueued after it returns; calls already
  * enqueued keep their grids. Errors: KVM_EINVAL (null ctx, max_workgroups < 0). */

@@ -25,16 +25,23 @@ namespace {
 constexpr int64_t kMaxSeqs = int64_t(1) << 20;
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxDescs = int64_t(1) << 32;
-// Target bytes per merge tile; rows per tile = max(1, this / row_bytes). Rows
-// shorter than kMergeShortRow take twice the tile and twice the bytes in
-// flight per workgroup: measured on MI355X, MLA's 1152-byte rows move 2.6 %
-// more that way, while 4 KiB rows lose 1 %.
+// Merge tiles, rows per tile = max(1, tile bytes / row_bytes), all measured
+// on MI355X in one process on the same buffers:
+//  - rows of at least kMergeShortRow bytes: 64 KiB tiles, and a grid capped
+//    at kMergeWgsPerCu workgroups per CU, each walking several tiles. On the
+//    Llama layer loop (4 KiB rows, 16,640 tiles) the cap moves 6.7 % more
+//    than one workgroup per tile, with a much tighter spread; 32 or 48 KiB
+//    tiles change nothing. Pack and unpack lose under any cap, so they keep
+//    one workgroup per tile.
+//  - shorter rows: 50 KiB tiles (44 MLA rows of 1152 B) and one workgroup
+//    per tile. On the MLA loop: 6.31 TB/s, against 5.96 with 128 KiB tiles
+//    and 5.57 with 128 KiB tiles under the cap; with 1024-byte rows, or 32
+//    instead of 61 layers, the same choice gains 8-9 %. The tile size is
+//    not smooth in effect (56 rows: 5.91, 64 rows: 6.06 TB/s): 42 to 48
+//    rows are the good range in every geometry tried.
 constexpr int64_t kMergeTileBytes = 64 * 1024;
+constexpr int64_t kMergeShortTileBytes = 50 * 1024;
 constexpr int64_t kMergeShortRow = 2048;
-// Merge grid cap, in workgroups per CU: above it each workgroup walks several
-// tiles. Measured on MI355X (Llama layer loop, 16,640 tiles): 16 per CU moves
-// 6.7 % more than one workgroup per tile, with a much tighter spread; pack
-// and unpack lose under any cap, so they keep one workgroup per tile.
 constexpr int32_t kMergeWgsPerCu = 16;
 
 // Unpack tile orders (tiles sorted by destination block), one per distinct
@@ -429,7 +436,7 @@ int check_copy_list(kvm_ctx* ctx, hipStream_t st, uintptr_t dst_base, uint64_t d
 struct MergePlan {
     explicit MergePlan(int64_t rb)
         : row_bytes(rb), wide(rb < kMergeShortRow),
-          rows_per_tile(int32_t(std::max<int64_t>(1, (wide ? 2 : 1) * kMergeTileBytes / rb))),
+          rows_per_tile(int32_t(std::max<int64_t>(1, (wide ? kMergeShortTileBytes : kMergeTileBytes) / rb))),
           bits(uint64_t(rb))
     {
     }
@@ -464,8 +471,10 @@ struct MergePlan {
     int launch(kvm_ctx* ctx, hipStream_t st) const
     {
         const int unit = move_unit(bits);
-        const int32_t cap = kMergeWgsPerCu * ctx->num_cus;
-        const int32_t grid = ctx->max_wgs > 0 ? std::min(ctx->max_wgs, cap) : cap;
+        // short rows: one workgroup per tile unless a budget is set
+        const int32_t cap = wide ? 0 : kMergeWgsPerCu * ctx->num_cus;
+        const int32_t grid = ctx->max_wgs > 0 ? (cap ? std::min(ctx->max_wgs, cap) : ctx->max_wgs)
+                                              : cap;
         for (const kvm::MergeBatch& b : batches) {
             hipError_t e = kvm::launch_merge(unit, row_bytes, rows_per_tile, b, wide, grid, st);
             if (e != hipSuccess) return fail_hip(ctx, e, "k_merge launch");

@@ -19,9 +19,10 @@
 //                       others, uses multiply-high division by invariant
 //                       integers.
 //   k_merge             a tile is (request, chunk of rows); a row comes from
-//                       the strided hit slice or from the miss rows. The grid
-//                       is capped (16 workgroups per CU), and each workgroup
-//                       walks tiles i, i + grid, ...
+//                       the strided hit slice or from the miss rows. For rows
+//                       of 2 KiB and more the grid is capped (16 workgroups
+//                       per CU) and each workgroup walks tiles i, i + grid,
+//                       ...; shorter rows take one workgroup per tile.
 //   k_bc_*              batched copy: per-group byte sums (64 objects per
 //                       wavefront), one exclusive scan, then a fixed grid in
 //                       which every wavefront copies an equal share of the
@@ -211,19 +212,23 @@ __device__ __forceinline__ void copy_elements(uint32_t total, Addr addr)
 
 // Workgroup shapes and element orders, chosen by measurement on MI355X (all
 // variants timed in one process on the same buffers, interleaved): pack and
-// merge keep a whole 64 KiB tile in flight per workgroup, pack in wave-major
-// order (+2.4 % over thread-major), merge in thread-major order (wave-major
-// costs it 18 %). Unpack, whose stores land on scattered pool objects, takes
+// merge keep a whole tile in flight per workgroup (64 KiB; about 50 KiB for
+// merge rows under 2 KiB, with 1024 x 8 slots: 1024 x 4 would need two
+// passes and loses 6 %), pack in wave-major order (+2.4 % over
+// thread-major), merge in thread-major order (wave-major costs it 18 %).
+// Unpack, whose stores land on scattered pool objects, takes
 // 576 threads x 8 units for items of up to 2048 units (the 32 KiB side of a
 // Llama block: 5.83 TB/s, against 5.56 at 256 x 8 and 5.58 at 1024 x 8) and
 // 1024 x 8 for larger items (a 72 KiB MLA block: 6.11 TB/s against 5.53 at
 // 576 x 8). The fused kernel takes 1024 x 8 for every size (+2 % on Llama,
-// +7 % on MLA against 576 x 8). No occupancy cap helps either.
+// +7 % on MLA against 576 x 8; 768 x 6 and 512 x 9, which fit a 72 KiB MLA
+// item exactly, lose 7 %), with split stores above 2048 units. No occupancy
+// cap helps either.
 constexpr int kPackBS = 1024, kPackUnroll = 4;
 constexpr bool kPackWaveMajor = true;
 constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
-constexpr int kMergeWideUnroll = 8;  // short rows: 128 KiB tiles, 1024 x 8 in flight
+constexpr int kMergeWideUnroll = 8;  // short rows: ~50 KiB tiles, 1024 x 8 slots
 constexpr int kUnpackBS = 576, kUnpackUnroll = 8;
 constexpr bool kUnpackWaveMajor = false;
 constexpr int kUnpackWideBS = 1024, kUnpackWideUnroll = 8;
@@ -307,8 +312,11 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
 // slots (as k_unpack) and into the request's output rows t0..t0+rows (as the
 // hit part of k_merge). Same work items, order and element order as k_unpack;
 // the second store of element j (row r, column c) of side s goes to
-// out + (t0 + r)*out_stride + s*row_bytes + c*U.
-template <int U, int BS, int UNR, bool WM>
+// out + (t0 + r)*out_stride + s*row_bytes + c*U. SPLIT issues a batch's pool
+// stores before its output stores rather than the two stores of each element
+// in turn (measured on MI355X: +2-4.5 % on 1152- and 1024-byte MLA rows,
+// -1.2 % on Llama's 2 KiB block sides).
+template <int U, int BS, int UNR, bool WM, bool SPLIT>
 __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restrict__ pool,
                                                      int32_t layer, const LayerBatch batch,
                                                      const int32_t* __restrict__ order,
@@ -348,12 +356,21 @@ __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restric
                     op[k] = out + int64_t(r) * s.out_stride + int64_t(c) * U;
                 }
             }
+            if constexpr (SPLIT) {
 #pragma unroll
-            for (int k = 0; k < UNR; ++k) {
-                const uint32_t j = base + k * kStep;
-                if (j < total) {
-                    st(reinterpret_cast<V*>(dp[k]), v[k]);
-                    st(reinterpret_cast<V*>(op[k]), v[k]);
+                for (int k = 0; k < UNR; ++k)
+                    if (base + k * kStep < total) st(reinterpret_cast<V*>(dp[k]), v[k]);
+#pragma unroll
+                for (int k = 0; k < UNR; ++k)
+                    if (base + k * kStep < total) st(reinterpret_cast<V*>(op[k]), v[k]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < UNR; ++k) {
+                    const uint32_t j = base + k * kStep;
+                    if (j < total) {
+                        st(reinterpret_cast<V*>(dp[k]), v[k]);
+                        st(reinterpret_cast<V*>(op[k]), v[k]);
+                    }
                 }
             }
         }
@@ -624,9 +641,15 @@ __global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__
     }
 
 // Grid of a tile kernel: one workgroup per work item, or the budget if smaller.
+// A dispatch counts its grid in work-items, as a 32-bit number, so a grid of
+// 1024-thread workgroups holds at most this many. Every tile kernel walks its
+// items grid-stride, so a larger item count only gives each workgroup more.
+constexpr int64_t kMaxGridWgs = int64_t(0xFFFFFFFFu) / 1024;
+
 static dim3 tile_grid(int64_t ntiles, int32_t max_wgs)
 {
-    return dim3(uint32_t(max_wgs > 0 ? std::min<int64_t>(ntiles, max_wgs) : ntiles));
+    const int64_t n = max_wgs > 0 ? std::min<int64_t>(ntiles, max_wgs) : ntiles;
+    return dim3(uint32_t(std::min(n, kMaxGridWgs)));
 }
 
 hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t num_layers,
@@ -685,8 +708,13 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
 {
     const FastDiv dv = make_fastdiv(uint32_t(g.row_bytes / unit));
     const dim3 grid = tile_grid(b.tile0[b.n] * g.sides, max_wgs);
+    if (unit == 16 && int64_t(g.block_tokens) * (g.row_bytes / 16) > kUnpackWideItem) {
+        hipLaunchKernelGGL((k_unpack_merge<16, kFusedBS, kFusedUnroll, kFusedWaveMajor, true>),
+                           grid, dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err);
+        return hipGetLastError();
+    }
 #define KVM_FUSED(U)                                                                        \
-    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, kFusedWaveMajor>), grid,   \
+    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, kFusedWaveMajor, false>), grid, \
                        dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err)
     KVM_UNIT_SWITCH(unit, KVM_FUSED)
 #undef KVM_FUSED

@@ -122,8 +122,8 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
 hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* count_scratch,
                                int32_t* order, hipStream_t st);
 
-// wide: 16-byte moves keep 1024 x 8 units in flight per workgroup (for tiles
-// of 128 KiB) instead of 1024 x 4.
+// wide (rows under 2 KiB, tiles of about 50 KiB): 16-byte moves take 1024 x 8
+// unit slots per workgroup instead of 1024 x 4, so a tile fits one pass.
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
                         bool wide, int32_t max_wgs, hipStream_t st);
 
