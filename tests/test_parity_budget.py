@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import (SENTINEL, down, run_batch_copy, run_merge, run_pack_unpack,
-                      run_unpack_merge, say, up)
+from gpu_util import (SENTINEL, case_seed, down, run_batch_copy, run_merge,
+                      run_pack_unpack, run_unpack_merge, say, up)
 from paged_kv_cache_kvm_amd import kvmove as kv
 from paged_kv_cache_kvm_amd import workloads as wl
 
@@ -45,7 +45,7 @@ def budget_ctx(ctx, request):
 def test_budget_pack_unpack(budget_ctx, gpu, case):
     L, S, N, B, rb, Ts, kind = case
     run_pack_unpack(budget_ctx, gpu, L, S, N, B, rb, Ts, kind=kind,
-                    seed=hash(str(case)) & 0xFFFF)
+                    seed=case_seed(case))
 
 
 @pytest.mark.parametrize("budget_ctx", BUDGETS, indirect=True)
@@ -57,7 +57,7 @@ def test_budget_pack_unpack(budget_ctx, gpu, case):
 def test_budget_merge(budget_ctx, gpu, case):
     C, reqs, L, hp, mp, op, off = case
     run_merge(budget_ctx, gpu, C, reqs, L=L, hit_pad=hp, miss_pad=mp, out_pad=op, offset=off,
-              seed=hash(str(case)) & 0xFFFF)
+              seed=case_seed(case))
 
 
 @pytest.mark.parametrize("budget_ctx", BUDGETS, indirect=True)
@@ -70,7 +70,7 @@ def test_budget_merge(budget_ctx, gpu, case):
 def test_budget_unpack_merge(budget_ctx, gpu, case):
     L, S, N, B, rb, reqs, kind = case
     run_unpack_merge(budget_ctx, gpu, L, S, N, B, rb, reqs, kind=kind,
-                     seed=hash(str(case)) & 0xFFFF)
+                     seed=case_seed(case))
 
 
 @pytest.mark.parametrize("budget_ctx", BUDGETS, indirect=True)
