@@ -602,12 +602,14 @@ def host_cpu():
     return model, len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(wl, reps=12):
+def cpu_baseline(wl, reps=12, host_threads=16):
     """The oracle on the host cores, on request 0 of the same workload: its 32
     unpack_layer + merge_layer calls and its pack_full (1/8 of a step). The
     request's 2080 blocks sit in a host pool of exactly that many blocks under
     a random permutation table (the same random 32 KiB object accesses without
-    a 48 GiB host pool); every page is touched before timing."""
+    a 48 GiB host pool); every page is touched before timing. Timed on one
+    thread, then from up to host_threads threads (a GPU's share of the host)
+    over disjoint parts of the same sample."""
     import numpy as np
     import oracle
     w = wl.LLAMA8B
@@ -632,19 +634,50 @@ def cpu_baseline(wl, reps=12):
                                complete[l * t_all * C:], C)
         oracle.pack_full(pool, ref, L, table, t_all, packed)
 
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        sample()
-        times.append(time.perf_counter() - t0)
-    dt = statistics.median(times)
-    nbytes = L * 2 * t_hit * C + L * 2 * t_all * C + 2 * t_all * L * C
     model, threads = host_cpu()
+    nthreads = max(1, min(threads, host_threads))
+    per = -(-N // nthreads)                  # blocks of each thread's pack_full share
+    spans = [(b * B, min(t_all, (b + per) * B)) for b in range(0, N, per)]
+
+    def layers_of(k):
+        for l in range(k, L, nthreads):      # disjoint pool layers and complete_layer rows
+            oracle.unpack_layer(pool, ref, L, l, table, t_hit, fb)
+            oracle.merge_layer(C, fb[l * C:], L * C, t_hit, miss[l * C:], L * C, t_miss,
+                               complete[l * t_all * C:], C)
+
+    def pack_span(span):                     # a block-aligned token range is a sequence
+        t0, t1 = span
+        oracle.pack_full(pool, ref, L, table[t0 // B:-(-t1 // B)], t1 - t0,
+                         packed[t0 * L * C:t1 * L * C])
+
+    def sample_threaded(ex):
+        list(ex.map(layers_of, range(min(nthreads, L))))
+        list(ex.map(pack_span, spans))
+
+    def timed(fn, *a):
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn(*a)
+            times.append(time.perf_counter() - t0)
+        return statistics.median(times), sum(times)
+
+    nbytes = L * 2 * t_hit * C + L * 2 * t_all * C + 2 * t_all * L * C
+    dt, total = timed(sample)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(nthreads) as ex:   # ctypes calls release the GIL
+        dt_mt, total_mt = timed(sample_threaded, ex)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"request 0 of 8 ({L} unpack_layer + {L} merge_layer + pack_full, "
-                      f"{nbytes / 1e9:.1f} GB), median of {reps} runs ({sum(times):.1f} s), "
+                      f"{nbytes / 1e9:.1f} GB), median of {reps} runs ({total:.1f} s), "
                       f"single thread, host pool of the request's {N} blocks",
-            "host": f"{model}; {threads} hardware threads available"}
+            "host": f"{model}; {threads} hardware threads available",
+            "threaded": {"value": round(nbytes / dt_mt / 1e9, 3), "unit": "GB/s",
+                         "cores": nthreads,
+                         "sample": f"the same sample, median of {reps} runs ({total_mt:.1f} s): "
+                                   f"the unchanged oracle called from {nthreads} threads, "
+                                   f"unpack_layer + merge_layer split by layer, pack_full by "
+                                   f"block-aligned token ranges"}}
 
 
 PROFILE = os.path.join(ROOT, "profiles", "llama8b_layer_loop_hbm_traffic.md")
