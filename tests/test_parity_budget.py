@@ -53,7 +53,8 @@ def test_budget_pack_unpack(budget_ctx, gpu, case):
     # (C, reqs, L, hit_pad, miss_pad, out_pad, offset)
     (4096, [(300, 20), (0, 9), (13, 0), (0, 0), (64, 64)], 32, 0, 0, 0, 0),
     (36, [(5, 3)] * 90, 3, 4, 12, 28, 0),
-], ids=["llama-rows", "many-reqs"])
+    (1152, [(1000, 77), (300, 5)], 61, 0, 0, 0, 0),  # short 16-byte rows: ~50 KiB tiles
+], ids=["llama-rows", "many-reqs", "mla-rows"])
 def test_budget_merge(budget_ctx, gpu, case):
     C, reqs, L, hp, mp, op, off = case
     run_merge(budget_ctx, gpu, C, reqs, L=L, hit_pad=hp, miss_pad=mp, out_pad=op, offset=off,
@@ -66,7 +67,8 @@ def test_budget_merge(budget_ctx, gpu, case):
     (3, 2, 200, 16, 512, [(300, 20), (0, 9), (13, 0), (0, 0), (64, 64)], "dense"),
     (2, 2, 700, 3, 48, [(5, 2), (1, 1)] * 70, "block_major"),
     (2, 3, 100, 4, 32, [(23, 5), (9, 0), (0, 3)], "dense"),     # three sides
-], ids=["mixed", "many-reqs", "three-sides"])
+    (3, 1, 300, 64, 1152, [(700, 77), (65, 3)], "slot"),        # wide items: split stores
+], ids=["mixed", "many-reqs", "three-sides", "mla-slot"])
 def test_budget_unpack_merge(budget_ctx, gpu, case):
     L, S, N, B, rb, reqs, kind = case
     run_unpack_merge(budget_ctx, gpu, L, S, N, B, rb, reqs, kind=kind,
