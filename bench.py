@@ -427,7 +427,7 @@ def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
             "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
 
 
-def mla_section(torch, kv, wl, ctx, dev, reps=3):
+def mla_section(torch, kv, wl, ctx, dev, reps=5):
     """The MLA agentic layer loop (64 requests, T_hit ~ U{16384..65536},
     T_miss ~ U{128..1024}, 61 layers of one 576-element bf16 latent, B=64, a
     one-layer slot pool): per layer unpack + merge into a 2-deep complete_layer
@@ -492,7 +492,10 @@ def mla_section(torch, kv, wl, ctx, dev, reps=3):
             ev.around(name, fn)
         torch.cuda.synchronize()
         ms = ev.mean_ms(name)
-        out[name] = {"ms_per_loop": round(ms, 3), "bytes_per_loop": nbytes,
+        all_ms = ev.all_ms(name)
+        out[name] = {"ms_per_loop": round(ms, 3),
+                     "ms_p10_p50_p90": [round(quantile(all_ms, q), 3) for q in (0.1, 0.5, 0.9)],
+                     "repetitions": reps, "bytes_per_loop": nbytes,
                      "GBps": round(nbytes / (ms * 1e6), 1),
                      "pct_hbm_peak": round(100 * nbytes / (ms * 1e6) / HBM_PEAK_GBS, 2)}
     assert ctx.take_device_errors() == 0
