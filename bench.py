@@ -418,11 +418,13 @@ def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
                                                           w.src_arena, descs, len(descs_np)))
     torch.cuda.synchronize()
     ms = ev.mean_ms("batch_copy")
+    spread = [round(quantile(ev.all_ms("batch_copy"), q), 4) for q in (0.1, 0.5, 0.9)]
     gbs = 2 * total / (ms * 1e6)
     del src, dst, descs
     torch.cuda.empty_cache()
     return {"workload": w.name, "objects": len(descs_np), "bytes_rw": 2 * total,
-            "ms_per_call": round(ms, 4), "GBps": round(gbs, 1),
+            "ms_per_call": round(ms, 4), "ms_p10_p50_p90": spread, "repetitions": reps,
+            "GBps": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
 
@@ -583,7 +585,10 @@ def restore_section(torch, kv, wl, ctx, dev, reps=10):
         torch.cuda.synchronize()
         ms = ev.mean_ms(name)
         gbs = 2 * total / (ms * 1e6)
-        out[name] = {"ms": round(ms, 4), "GBps": round(gbs, 1),
+        out[name] = {"ms": round(ms, 4),
+                     "ms_p10_p50_p90": [round(quantile(ev.all_ms(name), q), 4)
+                                        for q in (0.1, 0.5, 0.9)],
+                     "repetitions": reps, "GBps": round(gbs, 1),
                      "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                      "descriptors_per_s": round(n / (ms * 1e-3), 0)}
     assert ctx.take_device_errors() == 0
