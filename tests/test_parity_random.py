@@ -5,6 +5,8 @@ offsets, request counts and token counts, including empty requests; random
 merge row sizes and paddings; random copy lists with zero-length objects and
 arbitrary alignment. The oracle runs first in every runner, so a case that
 does not fit its buffers fails on the CPU before any kernel runs."""
+import os
+
 import numpy as np
 import pytest
 
@@ -14,6 +16,8 @@ from paged_kv_cache_kvm_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
+# cases per operation; a longer sweep: KVM_RANDOM_CASES=500
+CASES = int(os.environ.get("KVM_RANDOM_CASES", "40"))
 ROW_BYTES = [1, 2, 3, 5, 8, 12, 16, 24, 48, 64, 100, 256, 576, 1152, 2048]
 KINDS = ["dense", "block_major", "slot"]
 
@@ -21,7 +25,7 @@ KINDS = ["dense", "block_major", "slot"]
 def _paged_case(i):
     r = np.random.default_rng([2024, i])
     L, S = int(r.integers(1, 6)), int(r.integers(1, 5))
-    B, rb = int(r.integers(1, 21)), int(r.choice(ROW_BYTES))
+    B, rb = int(r.choice([*range(1, 21), 32, 64])), int(r.choice(ROW_BYTES))
     n = int(r.integers(1, 7))
     Ts = [int(t) for t in r.integers(0, 200, size=n)]
     N = sum(wl.blocks_needed(t, B) for t in Ts) + int(r.integers(1, 20))
@@ -39,16 +43,16 @@ def ctx(gpu):
     c.close()
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(CASES))
 def test_random_pack_unpack(ctx, gpu, i):
     L, S, N, B, rb, Ts, kind, bp, tp, off = _paged_case(i)
     run_pack_unpack(ctx, gpu, L, S, N, B, rb, Ts, kind=kind, block_pad=bp, ts_pad=tp, offset=off,
                     seed=3000 + i)
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(CASES))
 def test_random_unpack_merge(ctx, gpu, i):
-    L, S, N, B, rb, Ts, kind, _, tp, off = _paged_case(100 + i)
+    L, S, N, B, rb, Ts, kind, _, tp, off = _paged_case(100_000 + i)
     r = np.random.default_rng([2025, i])
     reqs = [(t, int(r.integers(0, 60))) for t in Ts]
     N = sum(wl.blocks_needed(h + m, B) for h, m in reqs) + 1
@@ -57,7 +61,7 @@ def test_random_unpack_merge(ctx, gpu, i):
                      offset=off, seed=4000 + i)
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(CASES))
 def test_random_merge(ctx, gpu, i):
     r = np.random.default_rng([2026, i])
     C = int(r.choice([1, 3, 16, 36, 100, 512, 1152, 4096, 5000]))
@@ -67,7 +71,7 @@ def test_random_merge(ctx, gpu, i):
               offset=int(r.choice([0, 0, 1, 8])), seed=5000 + i)
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(CASES))
 def test_random_batch_copy(ctx, gpu, i):
     r = np.random.default_rng([2027, i])
     n = int(r.integers(1, 3000))
