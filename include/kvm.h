@@ -266,10 +266,10 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  * t < num_tokens and side s:
  *     pool[layer][s][block_table[t / B]][t % B] <- full[t][layer][s]  (row_bytes)
  * Slot rows of tokens >= num_tokens (a partial last block shared with miss
- * tokens) are left as they were. One launch per 128 sequences; one workgroup
- * per (sequence, block, side) work item. Blocks run in ascending
- * destination-block order:
- * the first call with a given set of sequence records sorts them on the
+ * tokens) are left as they were. One launch per 128 sequences; a work item
+ * is one side of one or two consecutive blocks in ascending destination-block
+ * order, one workgroup each. The
+ * first call with a given set of sequence records sorts the blocks on the
  * stream (a counting sort over the pool's blocks, kept in the context for the
  * following layers; skipped when the pool has far more blocks than the call
  * has tiles). Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside

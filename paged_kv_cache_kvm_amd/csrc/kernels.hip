@@ -7,7 +7,9 @@
 //
 //   k_pack / k_unpack /  one workgroup per work item. A pack item is
 //   k_unpack_merge      (sequence, block, layer); an unpack or fused item is
-//                       (sequence, block, side).
+//                       one side of two consecutive tiles in destination
+//                       order (of one tile when a tile exceeds 2048 16-byte
+//                       units).
 //                       With a workgroup budget below the item count, the
 //                       grid is the budget and workgroup i takes items i,
 //                       i + grid, i + 2*grid, ... (this bounds how many CUs
@@ -134,42 +136,79 @@ __device__ __forceinline__ TileAt tile_at(const Batch& batch, int32_t per, int64
     return t;
 }
 
-// Work item i is side i % sides of tile order[i / sides] (a null order means
-// tile i / sides); workgroup blockIdx.x takes items blockIdx.x, + grid, ...
-// Under a workgroup budget one workgroup copies many items in turn, so the
-// next item's record and block id are fetched before the current item is
-// copied, and the order entry one item further ahead: the dependent metadata
-// loads then overlap a copy instead of sitting between two. With one
-// workgroup per item the loop body runs once.
-template <class Batch, class Body>
-__device__ __forceinline__ void walk_tiles(const Batch& batch, int32_t per, int32_t sides,
+// The tiles a work item covers: G consecutive entries of the tile order (the
+// last item of a launch may hold fewer), all on the same side.
+template <int G>
+struct Item {
+    TileAt t[G];
+    int32_t count;
+};
+
+template <int G>
+struct TileIdx {
+    int64_t v[G];  // tile indices; -1 past the launch's last tile
+};
+
+// Work item i is side i % sides of tiles order[G*p .. G*p + G) with
+// p = i / sides (a null order means tiles G*p ..); workgroup blockIdx.x takes
+// items blockIdx.x, + grid, ... Under a workgroup budget one workgroup copies
+// many items in turn, so the next item's records and block ids are fetched
+// before the current item is copied, and the order entries one item further
+// ahead: the dependent metadata loads then overlap a copy instead of sitting
+// between two. With one workgroup per item the loop body runs once.
+template <int G, class Batch, class Body>
+__device__ __forceinline__ void walk_items(const Batch& batch, int32_t per, int32_t sides,
                                            const int32_t* __restrict__ order, Body body)
 {
-    const int64_t n = batch.tile0[batch.n] * sides;
+    const int64_t nt = batch.tile0[batch.n];
+    const int64_t n = (G == 1 ? nt : (nt + G - 1) / G) * sides;
     const int64_t grid = gridDim.x;
-    auto tile_of = [&](int64_t i) {
-        const int64_t p = sides == 1 ? i : sides == 2 ? (i >> 1) : i / sides;
-        return order ? int64_t(order[p]) : p;
-    };
     auto side_of = [&](int64_t i) {
         return sides == 1 ? 0 : sides == 2 ? int32_t(i & 1) : int32_t(i % sides);
     };
+    auto tiles_of = [&](int64_t i) {
+        const int64_t p = (sides == 1 ? i : sides == 2 ? (i >> 1) : i / sides) * G;
+        TileIdx<G> x;
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+            x.v[q] = p + q < nt ? (order ? int64_t(order[p + q]) : p + q) : -1;
+        return x;
+    };
+    auto item_at = [&](const TileIdx<G>& x, int32_t side) {
+        Item<G> it;
+        it.count = 0;
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+            if (x.v[q] >= 0) {
+                it.t[q] = tile_at(batch, per, x.v[q], side);
+                it.count = q + 1;
+            }
+        return it;
+    };
     int64_t i = blockIdx.x;
     if (i >= n) return;
-    TileAt cur = tile_at(batch, per, tile_of(i), side_of(i));
-    int64_t next = i + grid < n ? tile_of(i + grid) : 0;
+    Item<G> cur = item_at(tiles_of(i), side_of(i));
+    TileIdx<G> next = tiles_of(i + grid < n ? i + grid : i);
     for (;;) {
         const bool more = i + grid < n;
-        TileAt nxt = cur;
-        if (more) nxt = tile_at(batch, per, next, side_of(i + grid));
+        Item<G> nxt = cur;
+        if (more) nxt = item_at(next, side_of(i + grid));
         const int64_t j = i + 2 * grid;
-        const int64_t after = j < n ? tile_of(j) : 0;
+        const TileIdx<G> after = tiles_of(j < n ? j : i);
         body(cur);
         if (!more) break;
         cur = nxt;
         next = after;
         i += grid;
     }
+}
+
+// One tile per work item.
+template <class Batch, class Body>
+__device__ __forceinline__ void walk_tiles(const Batch& batch, int32_t per, int32_t sides,
+                                           const int32_t* __restrict__ order, Body body)
+{
+    walk_items<1>(batch, per, sides, order, [&](const Item<1>& it) { body(it.t[0]); });
 }
 
 // Copy the `total` unit-sized elements of one tile with a workgroup of BS
@@ -216,26 +255,24 @@ __device__ __forceinline__ void copy_elements(uint32_t total, Addr addr)
 // merge rows under 2 KiB, with 1024 x 8 slots: 1024 x 4 would need two
 // passes and loses 6 %), pack in wave-major order (+2.4 % over
 // thread-major), merge in thread-major order (wave-major costs it 18 %).
-// Unpack, whose stores land on scattered pool objects, takes
-// 576 threads x 8 units for items of up to 2048 units (the 32 KiB side of a
-// Llama block: 5.83 TB/s, against 5.56 at 256 x 8 and 5.58 at 1024 x 8) and
-// 1024 x 8 for larger items (a 72 KiB MLA block: 6.11 TB/s against 5.53 at
-// 576 x 8). The fused kernel takes 1024 x 8 for every size (+2 % on Llama,
-// +7 % on MLA against 576 x 8; 768 x 6 and 512 x 9, which fit a 72 KiB MLA
-// item exactly, lose 7 %), with split stores above 2048 units. No occupancy
-// cap helps either.
+// Unpack and the fused kernel, whose stores land on scattered pool objects,
+// take two tiles per work item at 1024 x 4 (the two 32 KiB sides of a Llama
+// item in one pass; one tile per item at 576 x 8 was the best single-tile
+// shape, 1.2-1.6 % slower) and, for tiles above 2048 units (a 72 KiB MLA
+// block), one tile per item at 1024 x 8 (unpack: 6.11 TB/s against 5.53 at
+// 576 x 8; fused: +7 %; 768 x 6 and 512 x 9, an exact fit, lose 7 %), the
+// fused kernel then with split stores. No occupancy cap helps either.
 constexpr int kPackBS = 1024, kPackUnroll = 4;
 constexpr bool kPackWaveMajor = true;
 constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
 constexpr int kMergeWideUnroll = 8;  // short rows: ~50 KiB tiles, 1024 x 8 slots
-constexpr int kUnpackBS = 576, kUnpackUnroll = 8;
+constexpr int kUnpackBS = 1024, kUnpackUnroll = 4;
 constexpr bool kUnpackWaveMajor = false;
 constexpr int kUnpackWideBS = 1024, kUnpackWideUnroll = 8;
-constexpr int64_t kUnpackWideItem = 2048;  // 16-byte units per item above which unpack
-                                           // takes the wide shape
-constexpr int kFusedBS = 1024, kFusedUnroll = 8;
-constexpr bool kFusedWaveMajor = false;
+constexpr int64_t kUnpackWideItem = 2048;  // 16-byte units per tile above which unpack
+                                           // and the fused kernel take the wide shape
+constexpr int kFusedBS = 1024, kFusedUnroll = 4, kFusedWideUnroll = 8;
 
 // ---------------------------------------------------------------- pack ---
 // full[t][l][s] <- pool[l][s][bt[t / B]][t % B] for the tokens of one block
@@ -274,35 +311,87 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
 
 // -------------------------------------------------------------- unpack ---
 // pool[layer][side][bt[t / B]][t % B] <- full[t][layer][side] for the tokens
-// of one block below num_tokens. A work item is one side of one block tile:
-// B strided row pieces read, one contiguous object written (measured on
-// MI355X: 3 % faster than one item per block with both sides). Element j of
-// an item is row j / V, unit column j % V. Items are taken in the tiles'
-// order[] (sorted by destination block id, k_order_*), so the object stores
-// of concurrently running workgroups ascend through the pool instead of
-// landing at random. A null order keeps the tiles' own order.
-template <int U, int BS, int UNR, bool WM>
+// of a block below num_tokens. A work item is one side of G consecutive tiles
+// of the order: B strided row pieces read and one contiguous object written
+// per tile. Tiles are taken in order[] (sorted by destination block id,
+// k_order_*), so the object stores of concurrently running workgroups ascend
+// through the pool instead of landing at random, and the G objects of one
+// item are often adjacent. A null order keeps the tiles' own order. Element j
+// of an item belongs to its first tile below the first tile's element count,
+// else to the second; within a tile it is row j / V, unit column j % V.
+//
+// Measured on MI355X (Llama block sides of 32 KiB): one side per item is
+// 7.6 % faster than both sides of a block (each workgroup then writes one
+// object, not two far apart), and two consecutive tiles per item another
+// 1.2-1.6 % faster than one (1024 x 4; 512 x 8, 1024 x 2 and three or four
+// tiles per item are slower).
+
+// The G tiles' source and destination bases and element counts, and the
+// error count for tiles with bad block ids (once per tile, on side 0).
+template <int G>
+struct ItemSpan {
+    const char* src[G];
+    char* dst[G];
+    char* out[G];
+    int64_t src_stride[G];
+    int64_t out_stride[G];
+    uint32_t first_end;  // elements of the first tile
+    uint32_t total;
+};
+
+template <int G, class Batch>
+__device__ __forceinline__ ItemSpan<G> item_span(const PoolGeom& g, char* pool, int32_t layer,
+                                                 const Batch& batch, const Item<G>& it,
+                                                 uint32_t units, unsigned long long* err)
+{
+    static_assert(G == 1 || G == 2, "one or two tiles per work item");
+    ItemSpan<G> sp;
+    uint32_t count[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        count[q] = 0;
+        sp.src[q] = nullptr;
+        sp.dst[q] = nullptr;
+        sp.out[q] = nullptr;
+        sp.src_stride[q] = 0;
+        sp.out_stride[q] = 0;
+        if (q >= it.count) continue;
+        const TileAt& t = it.t[q];
+        if (bad_block(t.blk, g.num_blocks)) {
+            if (threadIdx.x == 0 && t.side == 0) atomicAdd(err, 1ull);
+            continue;
+        }
+        const auto& s = batch.rec[t.si];
+        const int64_t t0 = t.b * g.block_tokens;
+        count[q] = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0)) * units;
+        sp.src[q] = s.full + t0 * s.token_stride + (int64_t(layer) * g.sides + t.side) * g.row_bytes;
+        sp.dst[q] = pool + layer * g.layer_stride + t.side * g.side_stride + t.blk * g.block_stride;
+        sp.src_stride[q] = s.token_stride;
+        if constexpr (Batch::kHasOut) {
+            sp.out[q] = s.out + t0 * s.out_stride + int64_t(t.side) * g.row_bytes;
+            sp.out_stride[q] = s.out_stride;
+        }
+    }
+    sp.first_end = count[0];
+    sp.total = G == 1 ? count[0] : count[0] + count[G - 1];
+    return sp;
+}
+
+template <int U, int BS, int UNR, bool WM, int G>
 __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ pool, int32_t layer,
                                                const SeqBatch batch, const int32_t* __restrict__ order,
                                                FastDiv div_v, unsigned long long* err)
 {
-    walk_tiles(batch, 1, g.sides, order, [&](const TileAt& t) {
-        const SeqRec& s = batch.rec[t.si];
-        const int32_t blk = t.blk;
-        if (bad_block(blk, g.num_blocks)) {
-            if (threadIdx.x == 0 && t.side == 0) atomicAdd(err, 1ull);
-            return;
-        }
-        const int64_t t0 = t.b * g.block_tokens;
-        const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-        const char* src = s.full + t0 * s.token_stride +
-                          (int64_t(layer) * g.sides + t.side) * g.row_bytes;
-        char* dst = pool + layer * g.layer_stride + t.side * g.side_stride + blk * g.block_stride;
-        copy_elements<U, BS, UNR, WM>(rows * div_v.d, [&](uint32_t j, const char*& sp, char*& dp) {
-            const uint32_t r = fdiv(j, div_v);
-            const uint32_t c = j - r * div_v.d;
-            sp = src + int64_t(r) * s.token_stride + int64_t(c) * U;
-            dp = dst + int64_t(r) * g.row_bytes + int64_t(c) * U;
+    walk_items<G>(batch, 1, g.sides, order, [&](const Item<G>& it) {
+        const ItemSpan<G> sp = item_span<G>(g, pool, layer, batch, it, div_v.d, err);
+        copy_elements<U, BS, UNR, WM>(sp.total, [&](uint32_t j, const char*& s, char*& d) {
+            const bool second = G == 2 && j >= sp.first_end;
+            const uint32_t jj = second ? j - sp.first_end : j;
+            const uint32_t r = fdiv(jj, div_v);
+            const uint32_t c = jj - r * div_v.d;
+            s = (second ? sp.src[G - 1] : sp.src[0]) +
+                int64_t(r) * (second ? sp.src_stride[G - 1] : sp.src_stride[0]) + int64_t(c) * U;
+            d = (second ? sp.dst[G - 1] : sp.dst[0]) + int64_t(r) * g.row_bytes + int64_t(c) * U;
         });
     });
 }
@@ -315,58 +404,47 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
 // out + (t0 + r)*out_stride + s*row_bytes + c*U. SPLIT issues a batch's pool
 // stores before its output stores rather than the two stores of each element
 // in turn (measured on MI355X: +2-4.5 % on 1152- and 1024-byte MLA rows,
-// -1.2 % on Llama's 2 KiB block sides).
-template <int U, int BS, int UNR, bool WM, bool SPLIT>
+// -1.2 % on Llama's 2 KiB block sides). Two tiles per item: +1.2 % on Llama.
+template <int U, int BS, int UNR, bool SPLIT, int G>
 __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restrict__ pool,
                                                      int32_t layer, const LayerBatch batch,
                                                      const int32_t* __restrict__ order,
                                                      FastDiv div_v, unsigned long long* err)
 {
     typedef typename Unit<U>::T V;
-    walk_tiles(batch, 1, g.sides, order, [&](const TileAt& t) {
-        const LayerRec& s = batch.rec[t.si];
-        const int32_t blk = t.blk;
-        if (bad_block(blk, g.num_blocks)) {
-            if (threadIdx.x == 0 && t.side == 0) atomicAdd(err, 1ull);
-            return;
-        }
-        const int64_t t0 = t.b * g.block_tokens;
-        const uint32_t rows = uint32_t(min(int64_t(g.block_tokens), s.num_tokens - t0));
-        const uint32_t total = rows * div_v.d;
-        const char* src = s.full + t0 * s.token_stride +
-                          (int64_t(layer) * g.sides + t.side) * g.row_bytes;
-        char* dst = pool + layer * g.layer_stride + t.side * g.side_stride + blk * g.block_stride;
-        char* out = s.out + t0 * s.out_stride + int64_t(t.side) * g.row_bytes;
-        constexpr uint32_t kStep = WM ? 64 : BS;
-        const uint32_t first = WM ? (threadIdx.x >> 6) * (64 * UNR) + (threadIdx.x & 63) : threadIdx.x;
-        const uint32_t limit = WM ? total + BS * UNR : total;
-        for (uint32_t base = first; base < limit; base += BS * UNR) {
+    walk_items<G>(batch, 1, g.sides, order, [&](const Item<G>& it) {
+        const ItemSpan<G> sp = item_span<G>(g, pool, layer, batch, it, div_v.d, err);
+        const uint32_t total = sp.total;
+        for (uint32_t base = threadIdx.x; base < total; base += BS * UNR) {
             V v[UNR];
             char* dp[UNR];
             char* op[UNR];
 #pragma unroll
             for (int k = 0; k < UNR; ++k) {
-                const uint32_t j = base + k * kStep;
+                const uint32_t j = base + k * BS;
                 if (j < total) {
-                    const uint32_t r = fdiv(j, div_v);
-                    const uint32_t c = j - r * div_v.d;
-                    v[k] = ld(reinterpret_cast<const V*>(src + int64_t(r) * s.token_stride +
+                    const bool second = G == 2 && j >= sp.first_end;
+                    const uint32_t jj = second ? j - sp.first_end : j;
+                    const uint32_t r = fdiv(jj, div_v);
+                    const uint32_t c = jj - r * div_v.d;
+                    const int q = second ? G - 1 : 0;
+                    v[k] = ld(reinterpret_cast<const V*>(sp.src[q] + int64_t(r) * sp.src_stride[q] +
                                                          int64_t(c) * U));
-                    dp[k] = dst + int64_t(r) * g.row_bytes + int64_t(c) * U;
-                    op[k] = out + int64_t(r) * s.out_stride + int64_t(c) * U;
+                    dp[k] = sp.dst[q] + int64_t(r) * g.row_bytes + int64_t(c) * U;
+                    op[k] = sp.out[q] + int64_t(r) * sp.out_stride[q] + int64_t(c) * U;
                 }
             }
             if constexpr (SPLIT) {
 #pragma unroll
                 for (int k = 0; k < UNR; ++k)
-                    if (base + k * kStep < total) st(reinterpret_cast<V*>(dp[k]), v[k]);
+                    if (base + k * BS < total) st(reinterpret_cast<V*>(dp[k]), v[k]);
 #pragma unroll
                 for (int k = 0; k < UNR; ++k)
-                    if (base + k * kStep < total) st(reinterpret_cast<V*>(op[k]), v[k]);
+                    if (base + k * BS < total) st(reinterpret_cast<V*>(op[k]), v[k]);
             } else {
 #pragma unroll
                 for (int k = 0; k < UNR; ++k) {
-                    const uint32_t j = base + k * kStep;
+                    const uint32_t j = base + k * BS;
                     if (j < total) {
                         st(reinterpret_cast<V*>(dp[k]), v[k]);
                         st(reinterpret_cast<V*>(op[k]), v[k]);
@@ -683,22 +761,40 @@ hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* 
     return hipGetLastError();
 }
 
+// Tiles per unpack or fused work item: two, unless two tiles' elements would
+// not fit the 32-bit element index (tiles above 2^30 elements).
+static bool two_tiles(int64_t tile_units)
+{
+    return 2 * tile_units <= int64_t(INT32_MAX);
+}
+
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
                          int32_t layer, const SeqBatch& b, const int32_t* order,
                          unsigned long long* err, int32_t max_wgs, hipStream_t st)
 {
     (void)num_layers;
     const FastDiv dv = make_fastdiv(uint32_t(g.row_bytes / unit));
-    const dim3 grid = tile_grid(b.tile0[b.n] * g.sides, max_wgs);
-    if (unit == 16 && int64_t(g.block_tokens) * (g.row_bytes / 16) > kUnpackWideItem) {
-        hipLaunchKernelGGL((k_unpack<16, kUnpackWideBS, kUnpackWideUnroll, kUnpackWaveMajor>), grid,
-                           dim3(kUnpackWideBS), 0, st, g, pool, layer, b, order, dv, err);
+    const int64_t units = int64_t(g.block_tokens) * (g.row_bytes / unit);
+    const int64_t nt = b.tile0[b.n];
+    if (unit == 16 && units > kUnpackWideItem) {
+        hipLaunchKernelGGL((k_unpack<16, kUnpackWideBS, kUnpackWideUnroll, kUnpackWaveMajor, 1>),
+                           tile_grid(nt * g.sides, max_wgs), dim3(kUnpackWideBS), 0, st, g, pool,
+                           layer, b, order, dv, err);
         return hipGetLastError();
     }
+    if (two_tiles(units)) {
+        const dim3 grid = tile_grid((nt + 1) / 2 * g.sides, max_wgs);
 #define KVM_UNPACK(U)                                                                       \
-    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dv, err)
-    KVM_UNIT_SWITCH(unit, KVM_UNPACK)
+    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor, 2>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dv, err)
+        KVM_UNIT_SWITCH(unit, KVM_UNPACK)
 #undef KVM_UNPACK
+    } else {
+        const dim3 grid = tile_grid(nt * g.sides, max_wgs);
+#define KVM_UNPACK(U)                                                                       \
+    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor, 1>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dv, err)
+        KVM_UNIT_SWITCH(unit, KVM_UNPACK)
+#undef KVM_UNPACK
+    }
     return hipGetLastError();
 }
 
@@ -707,17 +803,27 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
                                unsigned long long* err, int32_t max_wgs, hipStream_t st)
 {
     const FastDiv dv = make_fastdiv(uint32_t(g.row_bytes / unit));
-    const dim3 grid = tile_grid(b.tile0[b.n] * g.sides, max_wgs);
-    if (unit == 16 && int64_t(g.block_tokens) * (g.row_bytes / 16) > kUnpackWideItem) {
-        hipLaunchKernelGGL((k_unpack_merge<16, kFusedBS, kFusedUnroll, kFusedWaveMajor, true>),
-                           grid, dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err);
+    const int64_t units = int64_t(g.block_tokens) * (g.row_bytes / unit);
+    const int64_t nt = b.tile0[b.n];
+    if (unit == 16 && units > kUnpackWideItem) {
+        hipLaunchKernelGGL((k_unpack_merge<16, kFusedBS, kFusedWideUnroll, true, 1>),
+                           tile_grid(nt * g.sides, max_wgs), dim3(kFusedBS), 0, st, g, pool,
+                           layer, b, order, dv, err);
         return hipGetLastError();
     }
+    if (two_tiles(units)) {
+        const dim3 grid = tile_grid((nt + 1) / 2 * g.sides, max_wgs);
 #define KVM_FUSED(U)                                                                        \
-    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, kFusedWaveMajor, false>), grid, \
-                       dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err)
-    KVM_UNIT_SWITCH(unit, KVM_FUSED)
+    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, false, 2>), grid, dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err)
+        KVM_UNIT_SWITCH(unit, KVM_FUSED)
 #undef KVM_FUSED
+    } else {
+        const dim3 grid = tile_grid(nt * g.sides, max_wgs);
+#define KVM_FUSED(U)                                                                        \
+    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, false, 1>), grid, dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err)
+        KVM_UNIT_SWITCH(unit, KVM_FUSED)
+#undef KVM_FUSED
+    }
     return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ struct MergeRec {
 // tile0[i] is the first tile of record i, ascending from 0; tile0[n] is the
 // launch's tile count. Every record owns at least one tile.
 struct SeqBatch {
+    static constexpr bool kHasOut = false;
     int32_t n;
     int64_t tile0[kRecsPerLaunch + 1];
     SeqRec rec[kRecsPerLaunch];
@@ -85,6 +86,7 @@ struct LayerRec {
 };
 
 struct LayerBatch {
+    static constexpr bool kHasOut = true;
     int32_t n;
     int64_t tile0[kRecsPerLaunch + 1];
     LayerRec rec[kRecsPerLaunch];
