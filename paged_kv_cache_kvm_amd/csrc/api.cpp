@@ -206,7 +206,7 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
             std::memset(&nb_, 0, sizeof(nb_));
         }
         kvm::SeqBatch& b = plan->batches.back();
-        // unpack launches one work item per (tile, side)
+        // unpack launches at most one work item per (tile, side)
         const int64_t items_per_tile = per_layer_tiles ? 1 : p->num_sides;
         if ((b.tile0[b.n] + tiles) * items_per_tile > kMaxTiles) return KVM_ERANGE;
         b.rec[b.n].block_table = s.block_table;

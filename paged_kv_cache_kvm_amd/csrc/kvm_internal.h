@@ -106,9 +106,10 @@ hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t nu
                        const SeqBatch& b, unsigned long long* err, int32_t max_wgs,
                        hipStream_t st);
 
-// One work item per (tile, side): item i is side i % sides of tile
-// order[i / sides]. order: a permutation of the batch's tiles made by
-// launch_unpack_order; null keeps the tiles' own order.
+// Work item i is side i % sides of tiles order[G*p .. G*p + G), p = i / sides,
+// with G = 2 (one tile for tiles above 2048 16-byte units). order: a
+// permutation of the batch's tiles made by launch_unpack_order; null keeps
+// the tiles' own order.
 hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_layers,
                          int32_t layer, const SeqBatch& b, const int32_t* order,
                          unsigned long long* err, int32_t max_wgs, hipStream_t st);
