@@ -52,13 +52,20 @@ constexpr int32_t kMergeWgsPerCu = 16;
 // ascending.
 constexpr int kOrderSlots = 16;
 
+// The latest unpack or fused launch on one stream that read a slot's order.
+struct OrderReader {
+    hipStream_t stream = nullptr;
+    hipEvent_t done = nullptr;
+};
+constexpr size_t kOrderReaders = 8;  // streams tracked per slot
+
 struct OrderSlot {
     std::vector<char> key;
     int32_t* order = nullptr;
     int64_t cap = 0;
-    hipEvent_t ready = nullptr;     // after the sort kernels
-    hipEvent_t last_use = nullptr;  // after the latest unpack that read it
-    hipStream_t stream = nullptr;   // where the sort ran
+    hipEvent_t ready = nullptr;         // after the sort kernels
+    std::vector<OrderReader> readers;   // per stream; an eviction waits for all
+    hipStream_t stream = nullptr;       // where the sort ran
     uint64_t used = 0;
     bool valid = false;
 };
@@ -226,7 +233,7 @@ void order_release(kvm_ctx* c)
     for (OrderSlot& o : c->orders) {
         dev_free(c, o.order, size_t(o.cap));
         if (o.ready) (void)hipEventDestroy(o.ready);
-        if (o.last_use) (void)hipEventDestroy(o.last_use);
+        for (OrderReader& r : o.readers) (void)hipEventDestroy(r.done);
         o = OrderSlot();
     }
     dev_free(c, c->d_count, size_t(c->count_cap));
@@ -243,6 +250,42 @@ std::vector<char> order_key(const kvm::SeqBatch& b, int64_t num_blocks)
     std::memcpy(p + sizeof(int64_t), b.tile0, sizeof(int64_t) * (b.n + 1));
     std::memcpy(p + sizeof(int64_t) * (b.n + 2), b.rec, sizeof(kvm::SeqRec) * b.n);
     return k;
+}
+
+// Wait on the host until every launch that read the slot's order has run.
+hipError_t wait_readers(const OrderSlot& o)
+{
+    for (const OrderReader& r : o.readers) {
+        const hipError_t e = hipEventSynchronize(r.done);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Note that a launch just enqueued on `st` reads the slot's order. One event
+// per stream: a single event would cover only the latest reader, and an
+// eviction could then rewrite the order while another stream still reads it.
+int note_reader(kvm_ctx* c, OrderSlot* o, hipStream_t st)
+{
+    OrderReader* r = nullptr;
+    for (OrderReader& x : o->readers)
+        if (x.stream == st) r = &x;
+    hipError_t e = hipSuccess;
+    if (!r && o->readers.size() == kOrderReaders) {
+        // every tracked reader done, so any of their events may be reused
+        if ((e = wait_readers(*o)) != hipSuccess) return fail_hip(c, e, "hipEventSynchronize");
+        r = &o->readers[0];
+        r->stream = st;
+    } else if (!r) {
+        OrderReader x;
+        if ((e = hipEventCreateWithFlags(&x.done, hipEventDisableTiming)) != hipSuccess)
+            return fail_hip(c, e, "hipEventCreateWithFlags");
+        x.stream = st;
+        o->readers.push_back(x);
+        r = &o->readers.back();
+    }
+    if ((e = hipEventRecord(r->done, st)) != hipSuccess) return fail_hip(c, e, "hipEventRecord");
+    return KVM_OK;
 }
 
 // The unpack order of batch b, sorting it on `st` if it is not cached.
@@ -266,18 +309,17 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     OrderSlot* o = &c->orders[0];
     for (OrderSlot& x : c->orders)
         if (x.used < o->used) o = &x;
-    if (o->valid) {  // its sort or an unpack reading it may still be in flight
+    if (o->valid) {  // its sort or launches reading it may still be in flight
         hipError_t e = hipEventSynchronize(o->ready);
-        if (e == hipSuccess) e = hipEventSynchronize(o->last_use);
+        if (e == hipSuccess) e = wait_readers(*o);
         if (e != hipSuccess) return fail_hip(c, e, "hipEventSynchronize");
         o->valid = false;
     }
     const int64_t ntiles = b.tile0[b.n];
     hipError_t e;
-    if (!o->ready) {
-        if ((e = hipEventCreateWithFlags(&o->ready, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&o->last_use, hipEventDisableTiming)) != hipSuccess)
-            return fail_hip(c, e, "hipEventCreateWithFlags");
+    if (!o->ready && (e = hipEventCreateWithFlags(&o->ready, hipEventDisableTiming)) != hipSuccess) {
+        o->ready = nullptr;
+        return fail_hip(c, e, "hipEventCreateWithFlags");
     }
     if (o->cap < ntiles) {
         dev_free(c, o->order, size_t(o->cap));
@@ -578,10 +620,9 @@ int kvm_ctx_reserve_unpack(kvm_ctx* ctx, int64_t max_tiles, int64_t max_pool_blo
     hipError_t e = hipDeviceSynchronize();  // no order or count array may be in use
     if (e != hipSuccess) return fail_hip(ctx, e, "hipDeviceSynchronize");
     for (OrderSlot& o : ctx->orders) {
-        if (!o.ready) {
-            if ((e = hipEventCreateWithFlags(&o.ready, hipEventDisableTiming)) != hipSuccess ||
-                (e = hipEventCreateWithFlags(&o.last_use, hipEventDisableTiming)) != hipSuccess)
-                return fail_hip(ctx, e, "hipEventCreateWithFlags");
+        if (!o.ready && (e = hipEventCreateWithFlags(&o.ready, hipEventDisableTiming)) != hipSuccess) {
+            o.ready = nullptr;
+            return fail_hip(ctx, e, "hipEventCreateWithFlags");
         }
         if (o.cap < max_tiles) {
             dev_free(ctx, o.order, size_t(o.cap));
@@ -708,9 +749,12 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
             e = kvm::launch_unpack(unit, g, static_cast<char*>(const_cast<void*>(pool)), num_layers,
                                    layer, b, orders[i] ? orders[i]->order : nullptr, ctx->d_err,
                                    ctx->max_wgs, st);
-            if (e == hipSuccess && orders[i]) e = hipEventRecord(orders[i]->last_use, st);
         }
         if (e != hipSuccess) return fail_hip(ctx, e, pack ? "k_pack launch" : "k_unpack launch");
+        if (!pack && orders[i]) {
+            const int rc = note_reader(ctx, orders[i], st);
+            if (rc != KVM_OK) return rc;
+        }
     }
     return KVM_OK;
 }
@@ -828,8 +872,11 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
         hipError_t e = kvm::launch_unpack_merge(unit, g, static_cast<char*>(pool), layer, hit[i],
                                                 orders[i] ? orders[i]->order : nullptr,
                                                 ctx->d_err, ctx->max_wgs, st);
-        if (e == hipSuccess && orders[i]) e = hipEventRecord(orders[i]->last_use, st);
         if (e != hipSuccess) return fail_hip(ctx, e, "k_unpack_merge launch");
+        if (orders[i]) {
+            rc = note_reader(ctx, orders[i], st);
+            if (rc != KVM_OK) return rc;
+        }
     }
     return miss.batches.empty() ? KVM_OK : miss.launch(ctx, st);
 }

@@ -369,3 +369,45 @@ def test_more_items_than_one_dispatch_holds(ctx, gpu):
     T = 4_300_000
     run_pack_unpack(ctx, gpu, 1, 1, T, 1, 16, [T], seed=11)
     run_unpack_merge(ctx, gpu, 1, 1, T + 100, 1, 16, [(T, 100)], kind="slot", seed=12)
+
+
+def test_order_eviction_waits_for_every_stream(gpu):
+    """A cached unpack order read on two streams, then evicted: the eviction
+    must wait for both readers. Stream a reads it slowly (a budget of one
+    workgroup), stream b reads it quickly and then brings 16 new record sets,
+    the last of which evicts the order while a may still be reading it."""
+    say("  order eviction with readers on two streams")
+    c = kv.Context(0)
+    try:
+        L, S, N, B, rb = 2, 2, 1200, 4, 64
+        layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+        ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+        rng = np.random.default_rng(71)
+        T = 4000                                   # 1000 blocks, read by one workgroup on a
+        tab = wl.block_tables(71, 1, N, [wl.blocks_needed(T, B)])[0]
+        fb_np = rng.integers(0, 256, T * L * S * rb, dtype=np.uint8)
+        small = [100 + i for i in range(16)]       # 16 other record sets, fewer tiles
+        want_a = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
+        oracle.unpack_layer(want_a, ref, L, 0, tab, T, fb_np)
+        want_c = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
+        for t in small:
+            oracle.unpack_layer(want_c, ref, L, 1, tab, t, fb_np)
+        bt, fb = up(tab, gpu), up(fb_np, gpu)
+        pool_a = up(np.full(L * S * N * B * rb, SENTINEL, np.uint8), gpu)
+        pool_b = up(np.full(L * S * N * B * rb, SENTINEL, np.uint8), gpu)
+        pool_c = up(np.full(L * S * N * B * rb, SENTINEL, np.uint8), gpu)
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        c.set_max_workgroups(1)
+        kv.kvm_unpack_layer(c.handle, layout, pool_a, L, 0, [kv.seq(bt, fb, T)], stream=a)
+        c.set_max_workgroups(0)
+        kv.kvm_unpack_layer(c.handle, layout, pool_b, L, 0, [kv.seq(bt, fb, T)], stream=b)
+        for t in small:
+            kv.kvm_unpack_layer(c.handle, layout, pool_c, L, 1, [kv.seq(bt, fb, t)], stream=b)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(pool_a), want_a), "slow reader on stream a"
+        assert np.array_equal(down(pool_b), want_a), "reader on stream b"
+        assert np.array_equal(down(pool_c), want_c), "the 16 evicting record sets"
+        assert c.take_device_errors() == 0
+    finally:
+        c.close()
