@@ -272,7 +272,9 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  * first call with a given set of sequence records sorts the blocks on the
  * stream (a counting sort over the pool's blocks, kept in the context for the
  * following layers; skipped when the pool has far more blocks than the call
- * has tiles). Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
+ * has tiles). The context keeps 16 such orders; a new record set beyond that
+ * replaces the least recently used one, and the call first waits on the host
+ * until every launch that read it, on any stream, has run. Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
  * [0, num_layers) or more than 2048 sequences with tokens in one call, and
  * KVM_ECHECK (checks on, kvm_ctx_set_checks). */
 int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
