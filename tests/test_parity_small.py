@@ -83,6 +83,8 @@ PACK_CASES = [
     (2, 2, 70000, 1, 16, [10, 3], "dense", 0, 0, 0),                    # pool >> tiles: own order
     (2, 3, 40, 4, 48, [33, 7], "dense", 0, 0, 0),                       # three sides
     (3, 5, 30, 2, 32, [19, 4, 1], "block_major", 0, 16, 0),             # five sides, padded tokens
+    (2, 2, 20, 256, 100, [1000, 257, 3], "dense", 0, 0, 0),              # 256-token blocks, 4-byte moves
+    (1, 1, 8, 1024, 16, [3000, 1025], "slot", 0, 0, 0),                 # 1024-token blocks
 ]
 
 
@@ -294,6 +296,8 @@ FUSED_CASES = [
     (2, 2, 60, 4, 5, [(23, 5), (9, 2)], "dense", 3, 1, 5, 1),                # byte moves
     (2, 3, 60, 4, 32, [(23, 5), (9, 0), (0, 3)], "dense", 0, 0, 16, 0),     # three sides
     (3, 5, 40, 2, 16, [(13, 2), (6, 1)], "slot", 16, 0, 0, 0),              # five sides
+    (2, 2, 24, 256, 100, [(1000, 30), (257, 0), (3, 5)], "dense", 0, 0, 0, 0),  # 256-token blocks
+    (1, 1, 10, 1024, 16, [(3000, 100), (1025, 1)], "slot", 0, 0, 16, 0),     # 1024-token blocks
 ]
 
 
