@@ -66,3 +66,18 @@ def test_header_compiles_as_c11_and_links(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, (out.returncode, out.stderr)
     assert out.stdout.split() == ["48", "32", "64", "72", "24"]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not installed")
+def test_readme_c_example_compiles(tmp_path):
+    """The README's C example compiles against include/kvm.h as C11 with
+    warnings as errors."""
+    import re
+    text = open(os.path.join(ROOT, "README.md")).read()
+    blocks = re.findall(r"```c\n(.*?)```", text, flags=re.S)
+    assert len(blocks) == 1
+    src = tmp_path / "example.c"
+    src.write_text(blocks[0])
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-c",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(tmp_path / "example.o")], check=True)
