@@ -777,8 +777,7 @@ def main():
         v["pct_of_copy_ceiling"] = round(100 * v["GBps"] / max(ceiling, stream_copy), 1)
     mla = None if args.no_mla else mla_section(torch, kv, wl, ctx, dev)
     bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
-    restore = None if args.no_batch_copy or args.no_restore else \
-        restore_section(torch, kv, wl, ctx, dev)
+    restore = None if args.no_restore else restore_section(torch, kv, wl, ctx, dev)
     small = None if args.no_small else small_call_section(torch, kv, wl, ctx, dev)
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
