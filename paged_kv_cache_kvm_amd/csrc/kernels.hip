@@ -585,6 +585,55 @@ __global__ __launch_bounds__(kBlock) void k_bc_group_sums(const CopyDesc* __rest
     if (lane == 0) group_sum[grp] = len;
 }
 
+// Lists of at most kSmallGroups groups take one workgroup for both steps:
+// its 16 wavefronts sum groups w, w + 16, ... (one coalesced load of 64
+// descriptors per group, four groups in flight per wavefront), then it scans
+// the sums, writing what k_bc_group_sums and k_exclusive_scan write together:
+// group_base[g] = the bytes of groups before g, group_base[ngroups] = total.
+// Per-layer restore calls and small calls then start their copy one launch
+// sooner.
+constexpr int64_t kSmallGroups = 1024;
+__global__ __launch_bounds__(1024) void k_bc_sums_scan(const CopyDesc* __restrict__ descs,
+                                                       int64_t n, uint64_t src_bytes,
+                                                       uint64_t dst_bytes,
+                                                       uint64_t* __restrict__ group_base,
+                                                       int64_t ngroups, unsigned long long* err)
+{
+    __shared__ unsigned long long sums[kSmallGroups];
+    __shared__ unsigned long long wave_total[16];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    for (int64_t g0 = wid; g0 < ngroups; g0 += 64) {
+        CopyDesc x[4];
+        unsigned long long len[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t k = (g0 + 16 * q) * kDescGroup + lane;
+            x[q] = CopyDesc{0, 0, 0};
+            if (g0 + 16 * q < ngroups && k < n) x[q] = descs[k];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            len[q] = object_bytes(x[q], src_bytes, dst_bytes);
+            if (len[q] != x[q].nbytes) atomicAdd(err, 1ull);
+            for (int o = 32; o > 0; o >>= 1) len[q] += __shfl_xor(len[q], o);
+            if (lane == 0 && g0 + 16 * q < ngroups) sums[g0 + 16 * q] = len[q];
+        }
+    }
+    __syncthreads();
+    const unsigned long long v = tid < ngroups ? sums[tid] : 0;
+    unsigned long long x = v;  // inclusive scan across the wavefront
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wave_total[wid] = x;
+    __syncthreads();
+    unsigned long long before = 0;
+    for (int w = 0; w < wid; ++w) before += wave_total[w];
+    if (tid < ngroups) group_base[tid] = before + x - v;
+    if (tid == 1023) group_base[ngroups] = before + x;
+}
+
 // Copy `len` bytes with one wavefront. When source and destination agree
 // modulo 16 the body moves as 16-byte vectors, kCopyUnroll per lane in flight;
 // when they agree modulo 4 as dwords; otherwise byte by byte.
@@ -850,6 +899,14 @@ hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uin
                              unsigned long long* err, hipStream_t st)
 {
     const int64_t ng = (n + kDescGroup - 1) / kDescGroup;
+    if (ng <= kSmallGroups) {
+        hipLaunchKernelGGL(k_bc_sums_scan, dim3(1), dim3(1024), 0, st, descs, n, src_bytes,
+                           dst_bytes, group_base, ng, err);
+        hipLaunchKernelGGL(k_bc_copy, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs, n,
+                           src, src_bytes, dst, dst_bytes, group_base, ng,
+                           uint64_t(large_blocks) * kWavesPerBlock);
+        return hipGetLastError();
+    }
     const uint32_t sum_blocks = uint32_t((ng + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL(k_bc_group_sums, dim3(sum_blocks), dim3(kBlock), 0, st, descs, n,
                        src_bytes, dst_bytes, group_sum, ng, err);
