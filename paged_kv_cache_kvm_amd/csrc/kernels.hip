@@ -26,9 +26,11 @@
 //                       per CU) and each workgroup walks tiles i, i + grid,
 //                       ...; shorter rows take one workgroup per tile.
 //   k_bc_*              batched copy: per-group byte sums (64 objects per
-//                       wavefront), one exclusive scan, then a fixed grid in
-//                       which every wavefront copies an equal share of the
-//                       total bytes, walking the objects its share covers.
+//                       wavefront), one exclusive scan (one workgroup does
+//                       both for lists of up to 1,024 groups), then a fixed
+//                       grid in which every wavefront copies an equal share
+//                       of the total bytes, walking the objects its share
+//                       covers.
 //
 // Page notation (DualPath KV Loading, key-objects table; Tutti reading notes,
 // prerequisites 3 and 5): T tokens, L layers, C_KV = sides * row_bytes per
@@ -211,11 +213,13 @@ __device__ __forceinline__ void walk_tiles(const Batch& batch, int32_t per, int3
     walk_items<1>(batch, per, sides, order, [&](const Item<1>& it) { body(it.t[0]); });
 }
 
-// Copy the `total` unit-sized elements of one tile with a workgroup of BS
+// Copy the `total` unit-sized elements of one work item with a workgroup of BS
 // threads: every thread issues UNR loads, then UNR stores, so a workgroup keeps
 // BS*UNR*U bytes in flight. addr(j, src, dst) names element j's two addresses;
-// consecutive j are consecutive bytes of a token row, so a wavefront's 64 lanes
-// always touch 64 adjacent units. Which elements a wavefront takes per batch:
+// consecutive j within a row are consecutive bytes of it, so a wavefront's 64
+// lanes touch adjacent units except where a row ends. total is at most
+// INT32_MAX (the host checks tile sizes), so no index below wraps. Which
+// elements a wavefront takes per batch:
 //   WAVE_MAJOR = false: element k of thread t is base + k*BS + t (a wavefront's
 //                       UNR pieces are BS elements apart);
 //   WAVE_MAJOR = true:  each wavefront owns 64*UNR consecutive elements.
@@ -483,8 +487,10 @@ __global__ __launch_bounds__(BS) void k_merge(int32_t rows_per_tile, const Merge
 // -------------------------------------------------- unpack tile order ---
 // A counting sort of one launch batch's unpack tiles by destination block id.
 // Measured on MI355X: writing the scattered 32 KiB pool objects in ascending
-// block order while the Full Block rows are read in whatever order that gives
-// is 6-7 % faster than the reverse. The sort is robust to any table contents:
+// block order, while the Full Block rows are read in whatever order that
+// gives, is 21 % faster than the tables' own order (one item per block side).
+// Tiles with equal keys may come out in any order; only repeated or bad ids
+// share a key. The sort is robust to any table contents:
 // an id outside [0, N) gets key N (its tile is skipped by k_unpack anyway),
 // and repeated ids share a key, so the result is always a permutation of the
 // batch's tiles.
