@@ -5,8 +5,8 @@ buffers are passed as integer device addresses or as torch tensors (their
 data_ptr); streams as a torch stream, an integer hipStream_t, or None for the
 current torch stream. Each call raises KvmError on a non-zero status.
 
-The library must be built (paged_kv_cache_kvm_amd/build.py); importing this
-module fails loudly if libkvmove.so is missing: there is no fallback path.
+The library must be built (paged_kv_cache_kvm_amd/build.py): the first call
+into it raises if libkvmove.so is missing, and there is no fallback path.
 """
 from __future__ import annotations
 
