@@ -1,0 +1,48 @@
+"""bench.py's command line on the CPU: more than one GPU is refused with a
+message before anything touches a device, and the helpers that shape the JSON
+line (quantiles, the profile-hash check) behave as documented."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert out.returncode == 2
+    assert "one GPU only" in out.stderr
+    assert out.stdout == ""
+
+
+def test_quantile_interpolates():
+    b = _bench()
+    xs = [4.0, 1.0, 3.0, 2.0]
+    assert b.quantile(xs, 0.0) == 1.0
+    assert b.quantile(xs, 1.0) == 4.0
+    assert abs(b.quantile(xs, 0.5) - 2.5) < 1e-12
+
+
+def test_traffic_only_for_matching_kernel_sources():
+    """The committed traffic summary is used only while the kernel sources hash
+    to the hash it records; a summary of other sources reports nothing."""
+    b = _bench()
+    got = b.measured_traffic("unpack_layer")
+    text = open(b.PROFILE).read()
+    import hashlib
+    h = hashlib.sha256()
+    for f in b.KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() in text:
+        assert isinstance(got, int) and got > 0
+    else:
+        assert got is None
