@@ -260,23 +260,38 @@ __device__ __forceinline__ void copy_elements(uint32_t total, Addr addr)
 // passes and loses 6 %), pack in wave-major order (+2.4 % over
 // thread-major), merge in thread-major order (wave-major costs it 18 %).
 // Unpack and the fused kernel, whose stores land on scattered pool objects,
-// take two tiles per work item at 1024 x 4 (the two 32 KiB sides of a Llama
-// item in one pass; one tile per item at 576 x 8 was the best single-tile
-// shape, 1.2-1.6 % slower) and, for tiles above 2048 units (a 72 KiB MLA
-// block), one tile per item at 1024 x 8 (unpack: 6.11 TB/s against 5.53 at
-// 576 x 8; fused: +7 %; 768 x 6 and 512 x 9, an exact fit, lose 7 %), the
-// fused kernel then with split stores. No occupancy cap helps either.
+// take two tiles per work item at 768 x 4 and, for tiles above 2048 units (a
+// 72 KiB MLA block), one tile per item at 1024 x 8 (unpack: 6.11 TB/s against
+// 5.53 at 576 x 8; fused: +7 %; 768 x 6 and 512 x 9, an exact fit, lose 7 %),
+// the fused kernel then with split stores. For the pairs, 768 threads beat
+// every neighbour: on Llama's 32 KiB block sides unpack gains 4-8 % over
+// 1024 x 4 (which beat one tile per item at 576 x 8 by 1.2-1.6 %), and on
+// 16-18 KiB block sides (64-wide heads, MLA rows, 8-token blocks) 33-47 %
+// (over four boxes: Llama +3.4 to +7.5 % on three, -1.7 % on one); 576, 640
+// and 896 threads lose 5-35 %. The fused kernel takes 768 x 4 too (+16-18 %
+// on 64-wide heads), except for pairs of more than 3072 units, which keep
+// 1024 x 4 (768 x 4 costs Llama's fused layer 0.4-1.1 %). No occupancy cap
+// helps either.
 constexpr int kPackBS = 1024, kPackUnroll = 4;
 constexpr bool kPackWaveMajor = true;
+// Smaller pack tiles take smaller workgroups, so that most slots of a pass
+// hold an element: 768 threads for tiles of 1537-3072 units (a 32 KiB tile:
+// +5 % over 1024 x 4 on 64-wide heads and on Llama with 8-token blocks), 512
+// for 1536 units or fewer (MLA's 18 KiB tile with 16-token blocks: +62 %).
+// Llama's 64 KiB tiles keep 1024 x 4 (every smaller shape loses 5-10 %).
+constexpr int kPackMidBS = 768, kPackSmallBS = 512;
+constexpr int64_t kPackMidUnits = 3072, kPackSmallUnits = 1536;
 constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
 constexpr int kMergeWideUnroll = 8;  // short rows: ~50 KiB tiles, 1024 x 8 slots
-constexpr int kUnpackBS = 1024, kUnpackUnroll = 4;
+constexpr int kUnpackBS = 768, kUnpackUnroll = 4;
 constexpr bool kUnpackWaveMajor = false;
 constexpr int kUnpackWideBS = 1024, kUnpackWideUnroll = 8;
 constexpr int64_t kUnpackWideItem = 2048;  // 16-byte units per tile above which unpack
                                            // and the fused kernel take the wide shape
-constexpr int kFusedBS = 1024, kFusedUnroll = 4, kFusedWideUnroll = 8;
+constexpr int kFusedBS = 768, kFusedUnroll = 4;
+constexpr int kFusedPairBS = 1024;  // pairs above 768 x 4 units (16-byte units)
+constexpr int kFusedWideBS = 1024, kFusedWideUnroll = 8;
 
 // ---------------------------------------------------------------- pack ---
 // full[t][l][s] <- pool[l][s][bt[t / B]][t % B] for the tokens of one block
@@ -327,8 +342,8 @@ __global__ __launch_bounds__(BS) void k_pack(PoolGeom g, const char* __restrict_
 // Measured on MI355X (Llama block sides of 32 KiB): one side per item is
 // 7.6 % faster than both sides of a block (each workgroup then writes one
 // object, not two far apart), and two consecutive tiles per item another
-// 1.2-1.6 % faster than one (1024 x 4; 512 x 8, 1024 x 2 and three or four
-// tiles per item are slower).
+// 1.2-1.6 % faster than one (then at 1024 x 4; 512 x 8, 1024 x 2 and three
+// or four tiles per item are slower), and 768 threads faster again.
 
 // The G tiles' source and destination bases and element counts, and the
 // error count for tiles with bad block ids (once per tile, on side 0).
@@ -792,10 +807,17 @@ hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t nu
     const uint32_t v = uint32_t(g.row_bytes / unit);
     const FastDiv dq = make_fastdiv(v * uint32_t(g.sides)), dv = make_fastdiv(v);
     const dim3 grid = tile_grid(b.tile0[b.n], max_wgs);
+    // elements of one tile: the workgroup that holds it in about one pass
+    const int64_t units = int64_t(g.block_tokens) * g.sides * v;
+#define KVM_PACK_BS(U, BS)                                                                  \
+    hipLaunchKernelGGL((k_pack<U, BS, kPackUnroll, kPackWaveMajor>), grid, dim3(BS), 0, st, g, pool, num_layers, b, dq, dv, err)
 #define KVM_PACK(U)                                                                         \
-    hipLaunchKernelGGL((k_pack<U, kPackBS, kPackUnroll, kPackWaveMajor>), grid, dim3(kPackBS), 0, st, g, pool, num_layers, b, dq, dv, err)
+    if (units > kPackMidUnits) KVM_PACK_BS(U, kPackBS);                                     \
+    else if (units > kPackSmallUnits) KVM_PACK_BS(U, kPackMidBS);                           \
+    else KVM_PACK_BS(U, kPackSmallBS)
     KVM_UNIT_SWITCH(unit, KVM_PACK)
 #undef KVM_PACK
+#undef KVM_PACK_BS
     return hipGetLastError();
 }
 
@@ -861,9 +883,17 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
     const int64_t units = int64_t(g.block_tokens) * (g.row_bytes / unit);
     const int64_t nt = b.tile0[b.n];
     if (unit == 16 && units > kUnpackWideItem) {
-        hipLaunchKernelGGL((k_unpack_merge<16, kFusedBS, kFusedWideUnroll, true, 1>),
-                           tile_grid(nt * g.sides, max_wgs), dim3(kFusedBS), 0, st, g, pool,
+        hipLaunchKernelGGL((k_unpack_merge<16, kFusedWideBS, kFusedWideUnroll, true, 1>),
+                           tile_grid(nt * g.sides, max_wgs), dim3(kFusedWideBS), 0, st, g, pool,
                            layer, b, order, dv, err);
+        return hipGetLastError();
+    }
+    if (unit == 16 && 2 * units > int64_t(kFusedBS) * kFusedUnroll) {
+        // a pair of 16-byte-unit tiles that one 768 x 4 pass does not hold
+        // (Llama's 32 KiB block sides) keeps 1024 x 4: one pass, +0.4-1.1 %
+        hipLaunchKernelGGL((k_unpack_merge<16, kFusedPairBS, kFusedUnroll, false, 2>),
+                           tile_grid((nt + 1) / 2 * g.sides, max_wgs), dim3(kFusedPairBS), 0, st,
+                           g, pool, layer, b, order, dv, err);
         return hipGetLastError();
     }
     if (two_tiles(units)) {
