@@ -597,6 +597,19 @@ def restore_section(torch, kv, wl, ctx, dev, reps=10):
     return out
 
 
+def device_info(torch):
+    """What the runtime reports of the GPU, to tell boxes apart when their
+    rates differ."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2**30, 1)}
+    for attr in ("clock_rate", "memory_clock_rate", "memory_bus_width"):
+        if hasattr(p, attr):
+            info[attr] = getattr(p, attr)
+    return info
+
+
 def host_cpu():
     """The host CPU's model name and the hardware threads this process may use."""
     model = "unknown"
@@ -810,6 +823,7 @@ def main():
         "batch_copy_restore": restore,
         "small_calls": small,
         "cpu_baseline": cpu,
+        "device": device_info(torch),
     }
     print(json.dumps(out), flush=True)
 
