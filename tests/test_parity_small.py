@@ -85,6 +85,8 @@ PACK_CASES = [
     (3, 5, 30, 2, 32, [19, 4, 1], "block_major", 0, 16, 0),             # five sides, padded tokens
     (2, 2, 20, 256, 100, [1000, 257, 3], "dense", 0, 0, 0),              # 256-token blocks, 4-byte moves
     (1, 1, 8, 1024, 16, [3000, 1025], "slot", 0, 0, 0),                 # 1024-token blocks
+    (2, 2, 64, 16, 1024, [300, 77], "dense", 0, 0, 0),                   # 2048-unit pack tiles
+    (3, 1, 80, 16, 1152, [301, 45], "slot", 0, 0, 0),                    # MLA rows, 16-token blocks
 ]
 
 
@@ -298,6 +300,7 @@ FUSED_CASES = [
     (3, 5, 40, 2, 16, [(13, 2), (6, 1)], "slot", 16, 0, 0, 0),              # five sides
     (2, 2, 24, 256, 100, [(1000, 30), (257, 0), (3, 5)], "dense", 0, 0, 0, 0),  # 256-token blocks
     (1, 1, 10, 1024, 16, [(3000, 100), (1025, 1)], "slot", 0, 0, 16, 0),     # 1024-token blocks
+    (2, 2, 64, 16, 1024, [(300, 20), (77, 3)], "dense", 0, 0, 0, 0),           # 64-wide heads
 ]
 
 
