@@ -279,8 +279,11 @@ constexpr bool kPackWaveMajor = true;
 // +5 % over 1024 x 4 on 64-wide heads and on Llama with 8-token blocks), 512
 // for 1536 units or fewer (MLA's 18 KiB tile with 16-token blocks: +62 %).
 // Llama's 64 KiB tiles keep 1024 x 4 (every smaller shape loses 5-10 %).
-constexpr int kPackMidBS = 768, kPackSmallBS = 512;
-constexpr int64_t kPackMidUnits = 3072, kPackSmallUnits = 1536;
+// Tiles of at most 768 units take 256 threads (8 KiB tiles of 512-byte rows
+// with 16-token blocks: +40 %); at 1024 units 256 x 4 was +6 % on one shape
+// and -2 % on another, so those keep 512.
+constexpr int kPackMidBS = 768, kPackSmallBS = 512, kPackTinyBS = 256;
+constexpr int64_t kPackMidUnits = 3072, kPackSmallUnits = 1536, kPackTinyUnits = 768;
 constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
 constexpr int kMergeWideUnroll = 8;  // short rows: ~50 KiB tiles, 1024 x 8 slots
@@ -291,6 +294,13 @@ constexpr int64_t kUnpackWideItem = 2048;  // 16-byte units per tile above which
                                            // and the fused kernel take the wide shape
 constexpr int kFusedBS = 768, kFusedUnroll = 4;
 constexpr int kFusedPairBS = 1024;  // pairs above 768 x 4 units (16-byte units)
+// A pair of 8 KiB tiles (at most 1024 units) leaves most of a 768 x 4 pass
+// idle: unpack takes 256 x 4 for it (+45-52 % on 512-byte rows with 16-token
+// blocks and 1 KiB rows with 8-token blocks), the fused kernel 512 x 4 (+2 to
+// +19 %; 256 x 4 ranged from -1 to +21 %). On 16 KiB tiles 512 x 4 loses 3-4 %
+// to 768 x 4, so the rule stops at 1024 units.
+constexpr int kUnpackSmallBS = 256, kFusedSmallBS = 512;
+constexpr int64_t kSmallPairUnits = 1024;
 constexpr int kFusedWideBS = 1024, kFusedWideUnroll = 8;
 
 // ---------------------------------------------------------------- pack ---
@@ -814,7 +824,8 @@ hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t nu
 #define KVM_PACK(U)                                                                         \
     if (units > kPackMidUnits) KVM_PACK_BS(U, kPackBS);                                     \
     else if (units > kPackSmallUnits) KVM_PACK_BS(U, kPackMidBS);                           \
-    else KVM_PACK_BS(U, kPackSmallBS)
+    else if (units > kPackTinyUnits) KVM_PACK_BS(U, kPackSmallBS);                          \
+    else KVM_PACK_BS(U, kPackTinyBS)
     KVM_UNIT_SWITCH(unit, KVM_PACK)
 #undef KVM_PACK
 #undef KVM_PACK_BS
@@ -861,10 +872,14 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
     }
     if (two_tiles(units)) {
         const dim3 grid = tile_grid((nt + 1) / 2 * g.sides, max_wgs);
+#define KVM_UNPACK_BS(U, BS)                                                                \
+    hipLaunchKernelGGL((k_unpack<U, BS, kUnpackUnroll, kUnpackWaveMajor, 2>), grid, dim3(BS), 0, st, g, pool, layer, b, order, dv, err)
 #define KVM_UNPACK(U)                                                                       \
-    hipLaunchKernelGGL((k_unpack<U, kUnpackBS, kUnpackUnroll, kUnpackWaveMajor, 2>), grid, dim3(kUnpackBS), 0, st, g, pool, layer, b, order, dv, err)
+    if (2 * units <= kSmallPairUnits) KVM_UNPACK_BS(U, kUnpackSmallBS);                     \
+    else KVM_UNPACK_BS(U, kUnpackBS)
         KVM_UNIT_SWITCH(unit, KVM_UNPACK)
 #undef KVM_UNPACK
+#undef KVM_UNPACK_BS
     } else {
         const dim3 grid = tile_grid(nt * g.sides, max_wgs);
 #define KVM_UNPACK(U)                                                                       \
@@ -898,10 +913,14 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
     }
     if (two_tiles(units)) {
         const dim3 grid = tile_grid((nt + 1) / 2 * g.sides, max_wgs);
+#define KVM_FUSED_BS(U, BS)                                                                 \
+    hipLaunchKernelGGL((k_unpack_merge<U, BS, kFusedUnroll, false, 2>), grid, dim3(BS), 0, st, g, pool, layer, b, order, dv, err)
 #define KVM_FUSED(U)                                                                        \
-    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, false, 2>), grid, dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err)
+    if (2 * units <= kSmallPairUnits) KVM_FUSED_BS(U, kFusedSmallBS);                       \
+    else KVM_FUSED_BS(U, kFusedBS)
         KVM_UNIT_SWITCH(unit, KVM_FUSED)
 #undef KVM_FUSED
+#undef KVM_FUSED_BS
     } else {
         const dim3 grid = tile_grid(nt * g.sides, max_wgs);
 #define KVM_FUSED(U)                                                                        \
