@@ -336,7 +336,11 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
  * counted (kvm_take_device_errors). Zero-length objects are no-ops. The bytes
  * are split evenly over the device's wavefronts (8 workgroups per CU, or 2
  * when the objects average 64 KiB or more and the call moves 1 GiB or more),
- * so a few large objects and many small ones balance alike. dst_base and
+ * so a few large objects and many small ones balance alike. A list of at most
+ * 64 objects is copied by one launch that uses none of the context's scratch
+ * (it allocates nothing and orders itself after no other stream's copy);
+ * longer lists first sum and scan their objects' sizes (one more launch, two
+ * above 65,536 objects) in the scratch. dst_base and
  * src_base may be the same buffer. Errors: KVM_EINVAL (null ctx, null
  * descs/bases with n_descs > 0, n_descs < 0), KVM_ERANGE (n_descs above 2^32),
  * KVM_ENOMEM, KVM_EHIP, KVM_ECHECK (checks on). */

@@ -896,9 +896,15 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
                                        src_bytes, descs, n_descs);
         if (rc != KVM_OK) return rc;
     }
+    // A list of one group (at most 64 objects) is copied in one launch that
+    // uses no group scratch: no allocation, and no wait on another stream's
+    // use of the scratch.
     const int64_t groups = (n_descs + kvm::kDescGroup - 1) / kvm::kDescGroup;
-    int rc = grow_groups(ctx, groups);
-    if (rc != KVM_OK) return rc;
+    const bool one_group = groups == 1;
+    if (!one_group) {
+        const int rc = grow_groups(ctx, groups);
+        if (rc != KVM_OK) return rc;
+    }
     // Enough wavefronts to cover every CU several times over, or the
     // workgroup budget if smaller; each takes an equal share of the bytes.
     // Lists of large objects use 2 workgroups per CU (within the budget).
@@ -907,15 +913,17 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     const int32_t large_blocks = std::min(copy_blocks, ctx->num_cus * 2);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (ctx->copy_pending && ctx->copy_stream != st) {
+    if (!one_group && ctx->copy_pending && ctx->copy_stream != st) {
         e = hipStreamWaitEvent(st, ctx->copy_done, 0);
         if (e != hipSuccess) return fail_hip(ctx, e, "hipStreamWaitEvent");
     }
     e = kvm::launch_batch_copy(
         static_cast<char*>(dst_base), dst_bytes, static_cast<const char*>(src_base), src_bytes,
-        reinterpret_cast<const CopyDesc*>(descs), n_descs, ctx->d_groups,
-        ctx->d_groups + ctx->group_cap, copy_blocks, large_blocks, ctx->d_err, st);
+        reinterpret_cast<const CopyDesc*>(descs), n_descs, one_group ? nullptr : ctx->d_groups,
+        one_group ? nullptr : ctx->d_groups + ctx->group_cap, copy_blocks, large_blocks,
+        ctx->d_err, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "batch copy launch");
+    if (one_group) return KVM_OK;
     e = hipEventRecord(ctx->copy_done, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "hipEventRecord");
     ctx->copy_stream = st;

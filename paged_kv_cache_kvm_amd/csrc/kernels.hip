@@ -722,6 +722,11 @@ __device__ __forceinline__ void wave_copy(const char* __restrict__ s, char* __re
 // objects in order until its share is done. An object larger than Q is split
 // across wavefronts; many small objects go to one wavefront.
 //
+// ONE_GROUP: a list of at most 64 objects is one group, so every wavefront
+// scans the group's lengths itself and takes the total from the scan; no
+// metadata launch runs before the copy and no group scratch is read, and the
+// first wavefront counts the invalid descriptors.
+//
 // When the objects average at least kLargeObject bytes and the call moves at
 // least kLargeCall bytes, only the first large_waves wavefronts take shares
 // (the rest exit at once). Measured on MI355X, 2 workgroups per CU instead of
@@ -730,15 +735,34 @@ __device__ __forceinline__ void wave_copy(const char* __restrict__ s, char* __re
 // objects, which are bound by walking descriptors, need every wavefront.
 constexpr uint64_t kLargeObject = 64 * 1024;
 constexpr uint64_t kLargeCall = uint64_t(1) << 30;
+template <bool ONE_GROUP>
 __global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__ descs, int64_t n,
                                                     const char* __restrict__ src,
                                                     uint64_t src_bytes, char* __restrict__ dst,
                                                     uint64_t dst_bytes,
                                                     const uint64_t* __restrict__ group_base,
-                                                    int64_t ngroups, uint64_t large_waves)
+                                                    int64_t ngroups, uint64_t large_waves,
+                                                    unsigned long long* err)
 {
     const int lane = threadIdx.x & 63;
-    const uint64_t total = group_base[ngroups];
+    auto inclusive_scan = [&](unsigned long long v) {
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long y = __shfl_up(v, o);
+            if (lane >= o) v += y;
+        }
+        return v;
+    };
+    unsigned long long len = 0, incl = 0;
+    uint64_t total;
+    if constexpr (ONE_GROUP) {
+        const CopyDesc x = lane < n ? descs[lane] : CopyDesc{0, 0, 0};
+        len = object_bytes(x, src_bytes, dst_bytes);
+        if (blockIdx.x == 0 && threadIdx.x < 64 && len != x.nbytes) atomicAdd(err, 1ull);
+        incl = inclusive_scan(len);
+        total = __shfl(incl, 63);
+    } else {
+        total = group_base[ngroups];
+    }
     const uint64_t all_waves = uint64_t(gridDim.x) * kWavesPerBlock;
     const uint64_t nwaves =
         total >= uint64_t(n) * kLargeObject && total >= kLargeCall
@@ -752,21 +776,21 @@ __global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__
     const uint64_t r1 = min(r0 + share, total);
 
     // last group whose first byte is <= r0
-    int64_t lo = 0, hi = ngroups - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (group_base[mid] <= r0) lo = mid;
-        else hi = mid - 1;
-    }
-    const int64_t k = lo * kDescGroup + lane;
-    unsigned long long len = k < n ? object_bytes(descs[k], src_bytes, dst_bytes) : 0;
-    unsigned long long incl = len;
-    for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+    int64_t lo = 0;
+    uint64_t rel = r0;
+    if constexpr (!ONE_GROUP) {
+        int64_t hi = ngroups - 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi + 1) >> 1;
+            if (group_base[mid] <= r0) lo = mid;
+            else hi = mid - 1;
+        }
+        const int64_t k = lo * kDescGroup + lane;
+        len = k < n ? object_bytes(descs[k], src_bytes, dst_bytes) : 0;
+        incl = inclusive_scan(len);
+        rel = r0 - group_base[lo];
     }
     const unsigned long long excl = incl - len;
-    const uint64_t rel = r0 - group_base[lo];
     const uint64_t owner = __ballot(excl <= rel && rel < incl);
     const int first = __ffsll((unsigned long long)owner) - 1;
     int64_t kk = lo * kDescGroup + first;
@@ -954,12 +978,17 @@ hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uin
                              unsigned long long* err, hipStream_t st)
 {
     const int64_t ng = (n + kDescGroup - 1) / kDescGroup;
+    const uint64_t large_waves = uint64_t(large_blocks) * kWavesPerBlock;
+    if (ng == 1) {
+        hipLaunchKernelGGL(k_bc_copy<true>, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs,
+                           n, src, src_bytes, dst, dst_bytes, nullptr, ng, large_waves, err);
+        return hipGetLastError();
+    }
     if (ng <= kSmallGroups) {
         hipLaunchKernelGGL(k_bc_sums_scan, dim3(1), dim3(1024), 0, st, descs, n, src_bytes,
                            dst_bytes, group_base, ng, err);
-        hipLaunchKernelGGL(k_bc_copy, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs, n,
-                           src, src_bytes, dst, dst_bytes, group_base, ng,
-                           uint64_t(large_blocks) * kWavesPerBlock);
+        hipLaunchKernelGGL(k_bc_copy<false>, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs,
+                           n, src, src_bytes, dst, dst_bytes, group_base, ng, large_waves, err);
         return hipGetLastError();
     }
     const uint32_t sum_blocks = uint32_t((ng + kWavesPerBlock - 1) / kWavesPerBlock);
@@ -968,9 +997,8 @@ hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uin
     hipLaunchKernelGGL(k_exclusive_scan<unsigned long long>, dim3(1), dim3(1024), 0, st,
                        reinterpret_cast<const unsigned long long*>(group_sum),
                        reinterpret_cast<unsigned long long*>(group_base), ng);
-    hipLaunchKernelGGL(k_bc_copy, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs, n, src,
-                       src_bytes, dst, dst_bytes, group_base, ng,
-                       uint64_t(large_blocks) * kWavesPerBlock);
+    hipLaunchKernelGGL(k_bc_copy<false>, dim3(uint32_t(copy_blocks)), dim3(kBlock), 0, st, descs, n,
+                       src, src_bytes, dst, dst_bytes, group_base, ng, large_waves, err);
     return hipGetLastError();
 }
 

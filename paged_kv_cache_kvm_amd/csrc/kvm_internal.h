@@ -130,9 +130,10 @@ hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* 
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
                         bool wide, int32_t max_wgs, hipStream_t st);
 
-// group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1. copy_blocks
-// workgroups are launched; when the objects average 64 KiB or more and total
-// 1 GiB or more, only the first large_blocks of them copy.
+// group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1; a list of at
+// most 64 objects uses neither (both may be null) and makes one launch.
+// copy_blocks workgroups are launched; when the objects average 64 KiB or more
+// and total 1 GiB or more, only the first large_blocks of them copy.
 hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uint64_t src_bytes,
                              const CopyDesc* descs, int64_t n, uint64_t* group_sum,
                              uint64_t* group_base, int32_t copy_blocks, int32_t large_blocks,

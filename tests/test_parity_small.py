@@ -188,6 +188,70 @@ def test_batch_copy_skips_out_of_range(ctx, gpu):
                    np.full(size, SENTINEL, np.uint8), d, expect_skipped=4, label="out of range")
 
 
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 129])
+def test_batch_copy_short_lists(ctx, gpu, n):
+    """Lists around the one-group limit (64 objects: one launch, no scratch),
+    with mixed alignments, zero lengths and two objects outside a buffer."""
+    rng = np.random.default_rng(27 + n)
+    lens = rng.integers(0, 20000, size=n)
+    lens[rng.integers(0, n)] = 0
+    arena = int(lens.sum()) + 64 * n + 4096
+    src_off = wl.placements(27, n, lens, arena, 1)
+    dst_off = wl.placements(28, n, lens, arena, 1)
+    d = _descs(src_off, dst_off, lens)
+    bad = 0
+    if n >= 2:
+        d[n - 1] = (arena - 5, 0, 6)             # source runs past its buffer
+        d[0] = (0, 2**64 - 16, 32)               # destination offset far out of range
+        bad = 2
+    run_batch_copy(ctx, gpu, rng.integers(0, 256, arena, dtype=np.uint8),
+                   np.full(arena, SENTINEL, np.uint8), d, expect_skipped=bad,
+                   label=f"short list n={n}")
+
+
+def test_batch_copy_short_list_uses_no_scratch(gpu):
+    """A list of at most 64 objects allocates nothing on a fresh context and
+    runs on a second stream beside a long list's copy on the first."""
+    c = kv.Context(0)
+    try:
+        before = c.device_bytes()
+        rng = np.random.default_rng(29)
+        src_np = rng.integers(0, 256, 1 << 20, dtype=np.uint8)
+        lens = np.full(64, 4096)
+        offs = 4096 * np.arange(64)
+        short = up(_descs(offs, offs[::-1].copy(), lens).view(np.uint8), gpu)
+        src = up(src_np, gpu)
+        dst = torch.full((1 << 20,), SENTINEL, dtype=torch.uint8, device=gpu)
+        kv.kvm_batch_copy(c.handle, dst, 1 << 20, src, 1 << 20, short, 64)
+        torch.cuda.synchronize()
+        assert c.device_bytes() == before
+        want = np.full(1 << 20, SENTINEL, np.uint8)
+        oracle.batch_copy(want, src_np, _descs(offs, offs[::-1].copy(), lens))
+        assert np.array_equal(down(dst), want)
+
+        long_lens = 256 * rng.integers(1, 64, size=3000)
+        arena = int(long_lens.sum()) + (1 << 20)
+        lsrc_np = rng.integers(0, 256, arena, dtype=np.uint8)
+        ld = _descs(wl.placements(30, 1, long_lens, arena), wl.placements(30, 2, long_lens, arena),
+                    long_lens)
+        lsrc, ldst = up(lsrc_np, gpu), torch.full((arena,), SENTINEL, dtype=torch.uint8, device=gpu)
+        ldesc = up(ld.view(np.uint8), gpu)
+        dst.fill_(SENTINEL)
+        a, b = torch.cuda.Stream(gpu), torch.cuda.Stream(gpu)
+        a.wait_stream(torch.cuda.current_stream())
+        b.wait_stream(torch.cuda.current_stream())
+        kv.kvm_batch_copy(c.handle, ldst, arena, lsrc, arena, ldesc, len(ld), stream=a)
+        kv.kvm_batch_copy(c.handle, dst, 1 << 20, src, 1 << 20, short, 64, stream=b)
+        torch.cuda.synchronize()
+        lwant = np.full(arena, SENTINEL, np.uint8)
+        oracle.batch_copy(lwant, lsrc_np, ld)
+        assert np.array_equal(down(ldst), lwant)
+        assert np.array_equal(down(dst), want)
+        assert c.take_device_errors() == 0
+    finally:
+        c.close()
+
+
 def test_raw_bits_survive(ctx, gpu):
     """bf16 NaN payloads, infinities, -0 and denormals come out bit-identical."""
     specials = np.array([0x7FC1, 0xFFFF, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x807F, 0x7FBF],
