@@ -260,18 +260,17 @@ __device__ __forceinline__ void copy_elements(uint32_t total, Addr addr)
 // passes and loses 6 %), pack in wave-major order (+2.4 % over
 // thread-major), merge in thread-major order (wave-major costs it 18 %).
 // Unpack and the fused kernel, whose stores land on scattered pool objects,
-// take two tiles per work item at 768 x 4 and, for tiles above 2048 units (a
-// 72 KiB MLA block), one tile per item at 1024 x 8 (unpack: 6.11 TB/s against
-// 5.53 at 576 x 8; fused: +7 %; 768 x 6 and 512 x 9, an exact fit, lose 7 %),
-// the fused kernel then with split stores. For the pairs, 768 threads beat
-// every neighbour: on Llama's 32 KiB block sides unpack gains 4-8 % over
-// 1024 x 4 (which beat one tile per item at 576 x 8 by 1.2-1.6 %), and on
-// 16-18 KiB block sides (64-wide heads, MLA rows, 8-token blocks) 33-47 %
-// (over four boxes: Llama +3.4 to +7.5 % on three, -1.7 % on one); 576, 640
-// and 896 threads lose 5-35 %. The fused kernel takes 768 x 4 too (+16-18 %
-// on 64-wide heads), except for pairs of more than 3072 units, which keep
-// 1024 x 4 (768 x 4 costs Llama's fused layer 0.4-1.1 %). No occupancy cap
-// helps either.
+// take two tiles per work item and, for tiles above 2048 units (a 72 KiB MLA
+// block), one tile per item at 1024 x 8 (unpack: 6.11 TB/s against 5.53 at
+// 576 x 8; fused: +7 %; 768 x 6 and 512 x 9, an exact fit, lose 7 %), the
+// fused kernel then with split stores. Pairs of more than 3072 units (Llama's
+// 32 KiB block sides) take 1024 x 4, one pass: 768 x 4 costs unpack 4.5-11 %
+// (two boxes, in one process and over alternating processes) and the fused
+// layer 0.4-1.1 %; 1024 x 4 pairs beat one tile per item at 576 x 8 by
+// 1.2-1.6 %. Pairs of 1025-3072 units (16-18 KiB block sides: 64-wide heads,
+// MLA rows, 8-token blocks) take 768 x 4, 33-47 % ahead of 1024 x 4 for
+// unpack and up to 17 % for the fused kernel; 576, 640 and 896 threads lose
+// 5-35 %. No occupancy cap helps either.
 constexpr int kPackBS = 1024, kPackUnroll = 4;
 constexpr bool kPackWaveMajor = true;
 // Smaller pack tiles take smaller workgroups, so that most slots of a pass
@@ -288,6 +287,7 @@ constexpr int kMergeBS = 1024, kMergeUnroll = 4;
 constexpr bool kMergeWaveMajor = false;
 constexpr int kMergeWideUnroll = 8;  // short rows: ~50 KiB tiles, 1024 x 8 slots
 constexpr int kUnpackBS = 768, kUnpackUnroll = 4;
+constexpr int kUnpackPairBS = 1024;  // pairs above 768 x 4 units, as kFusedPairBS
 constexpr bool kUnpackWaveMajor = false;
 constexpr int kUnpackWideBS = 1024, kUnpackWideUnroll = 8;
 constexpr int64_t kUnpackWideItem = 2048;  // 16-byte units per tile above which unpack
@@ -900,6 +900,7 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
     hipLaunchKernelGGL((k_unpack<U, BS, kUnpackUnroll, kUnpackWaveMajor, 2>), grid, dim3(BS), 0, st, g, pool, layer, b, order, dv, err)
 #define KVM_UNPACK(U)                                                                       \
     if (2 * units <= kSmallPairUnits) KVM_UNPACK_BS(U, kUnpackSmallBS);                     \
+    else if (2 * units > int64_t(kUnpackBS) * kUnpackUnroll) KVM_UNPACK_BS(U, kUnpackPairBS); \
     else KVM_UNPACK_BS(U, kUnpackBS)
         KVM_UNIT_SWITCH(unit, KVM_UNPACK)
 #undef KVM_UNPACK
