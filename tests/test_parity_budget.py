@@ -90,6 +90,24 @@ def test_budget_batch_copy(budget_ctx, gpu):
                    np.full(arena, SENTINEL, np.uint8), descs, label="mixed sizes, budget")
 
 
+@pytest.mark.parametrize("budget_ctx", BUDGETS, indirect=True)
+def test_budget_batch_copy_short_list(budget_ctx, gpu):
+    """40 objects (one launch, shares found by each wavefront's own scan), one
+    of them 4 MiB so that it spans many shares, and one out of range."""
+    rng = np.random.default_rng(78)
+    lens = rng.integers(0, 5000, size=40)
+    lens[7] = 4 << 20
+    arena = int(lens.sum()) + (1 << 16)
+    src_off = wl.placements(78, 1, lens, arena, 1)
+    dst_off = wl.placements(78, 2, lens, arena, 1)
+    descs = np.stack([src_off.astype(np.uint64), dst_off.astype(np.uint64),
+                      lens.astype(np.uint64)], axis=1)
+    descs[30] = (arena - 3, 0, 9)                 # source runs past its buffer
+    run_batch_copy(budget_ctx, gpu, rng.integers(0, 256, arena, dtype=np.uint8),
+                   np.full(arena, SENTINEL, np.uint8), descs, expect_skipped=1,
+                   label="short list, budget")
+
+
 @pytest.mark.parametrize("budget_ctx", [1, 2], indirect=True)
 def test_budget_bad_block_ids(budget_ctx, gpu):
     """A bad id skips its tile inside a workgroup's loop; the tiles after it in
