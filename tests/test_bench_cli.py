@@ -46,3 +46,35 @@ def test_traffic_only_for_matching_kernel_sources():
         assert isinstance(got, int) and got > 0
     else:
         assert got is None
+
+
+def test_profile_commands_run_committed_files_with_known_flags():
+    """Every rocprofv3 command quoted in profiles/ runs the repository's
+    bench.py with flags it accepts, and counter runs stay counter-only."""
+    import glob
+    import shlex
+    b = _bench()
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    assert files
+    seen = 0
+    for path in files:
+        cmds = [l.strip() for l in open(path) if "rocprofv3 --" in l and " -- " in l]
+        assert cmds, f"{os.path.basename(path)} quotes no rocprofv3 command"
+        for cmd in cmds:
+            tool, _, prog = cmd.partition(" -- ")
+            argv = shlex.split(prog)
+            assert argv[:3] == ["python", "-u", "<repo>/bench.py"], cmd
+            old = sys.argv
+            try:
+                sys.argv = ["bench.py", *argv[3:]]
+                args = b.parse()
+            finally:
+                sys.argv = old
+            assert args.gpus == 1 and args.steps >= 1, cmd
+            # counter runs take no API or memory trace domain alongside
+            assert "--pmc" not in tool or not any(
+                t in tool for t in ("--sys-trace", "--runtime-trace", "--hip-trace", "--hsa-trace",
+                                    "--memory-copy-trace", "--scratch-memory-trace",
+                                    "--marker-trace", " -s ", " -r ")), cmd
+            seen += 1
+    assert seen >= 4
