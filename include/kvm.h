@@ -273,8 +273,12 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  * stream (a counting sort over the pool's blocks, kept in the context for the
  * following layers; skipped when the pool has far more blocks than the call
  * has tiles). The context keeps 16 such orders; a new record set beyond that
- * replaces the least recently used one, and the call first waits on the host
- * until every launch that read it, on any stream, has run. Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
+ * replaces the least recently used one, after every launch that read it. While
+ * all of a context's unpack and fused calls use one stream, stream order
+ * provides that and nothing is recorded per call; the first call on a second
+ * stream waits on the host for the device once, and from then on each call
+ * records an event that a later replacement waits for on the host.
+ * Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
  * [0, num_layers) or more than 2048 sequences with tokens in one call, and
  * KVM_ECHECK (checks on, kvm_ctx_set_checks). */
 int kvm_unpack_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,
@@ -340,7 +344,9 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
  * 64 objects is copied by one launch that uses none of the context's scratch
  * (it allocates nothing and orders itself after no other stream's copy);
  * longer lists first sum and scan their objects' sizes (one more launch, two
- * above 65,536 objects) in the scratch. dst_base and
+ * above 65,536 objects) in the scratch. The first such call on a second
+ * stream waits on the host for the device once; from then on a call on
+ * another stream than the previous one waits, on the device, for that call. dst_base and
  * src_base may be the same buffer. Errors: KVM_EINVAL (null ctx, null
  * descs/bases with n_descs > 0, n_descs < 0), KVM_ERANGE (n_descs above 2^32),
  * KVM_ENOMEM, KVM_EHIP, KVM_ECHECK (checks on). */

@@ -433,6 +433,44 @@ def test_one_context_on_two_streams(gpu):
         c.close()
 
 
+def test_copy_scratch_second_stream_waits(gpu):
+    """Two lists that share the group scratch: the first, slow (one
+    workgroup), on stream a as the context's first copy, so it records no
+    event; the second on stream b right after it. The first call on b must
+    wait for a's copy before the scratch is rewritten."""
+    say("  batched copy: a second stream after a slow first copy")
+    c = kv.Context(0)
+    try:
+        rng = np.random.default_rng(73)
+        size = 1 << 24
+        src_np = rng.integers(0, 256, size, dtype=np.uint8)
+        src = up(src_np, gpu)
+        half = size // 2
+        lists = []
+        for k in range(2):
+            lens = 256 * rng.integers(1, 16, size=1500)
+            d = np.stack([wl.placements(73, 1 + k, lens, size),
+                          k * half + wl.placements(73, 3 + k, lens, half), lens],
+                         axis=1).astype(np.uint64)
+            lists.append(d)
+        want = np.full(size, SENTINEL, np.uint8)
+        for d in lists:
+            oracle.batch_copy(want, src_np, d)
+        dst = up(np.full(size, SENTINEL, np.uint8), gpu)
+        dd = [up(d.view(np.uint8), gpu) for d in lists]
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        c.set_max_workgroups(1)
+        kv.kvm_batch_copy(c.handle, dst, size, src, size, dd[0], len(lists[0]), stream=a)
+        c.set_max_workgroups(0)
+        kv.kvm_batch_copy(c.handle, dst, size, src, size, dd[1], len(lists[1]), stream=b)
+        torch.cuda.synchronize()
+        assert np.array_equal(down(dst), want)
+        assert c.take_device_errors() == 0
+    finally:
+        c.close()
+
+
 def test_more_items_than_one_dispatch_holds(ctx, gpu):
     """4.3 M one-token blocks of 16 bytes: pack, unpack and fused items beyond
     the 4,194,303 workgroups of 1024 threads a dispatch can count, so the
@@ -442,12 +480,16 @@ def test_more_items_than_one_dispatch_holds(ctx, gpu):
     run_unpack_merge(ctx, gpu, 1, 1, T + 100, 1, 16, [(T, 100)], kind="slot", seed=12)
 
 
-def test_order_eviction_waits_for_every_stream(gpu):
+@pytest.mark.parametrize("warm", [True, False], ids=["multi-stream", "second-stream"])
+def test_order_eviction_waits_for_every_stream(gpu, warm):
     """A cached unpack order read on two streams, then evicted: the eviction
     must wait for both readers. Stream a reads it slowly (a budget of one
     workgroup), stream b reads it quickly and then brings 16 new record sets,
-    the last of which evicts the order while a may still be reading it."""
-    say("  order eviction with readers on two streams")
+    the last of which evicts the order while a may still be reading it.
+    multi-stream: the context has already seen both streams, so each read
+    records its event; second-stream: the slow read is the context's first
+    call, recorded by no event, and the first call on b must wait for it."""
+    say(f"  order eviction with readers on two streams ({'warm' if warm else 'cold'})")
     c = kv.Context(0)
     try:
         L, S, N, B, rb = 2, 2, 1200, 4, 64
@@ -469,6 +511,11 @@ def test_order_eviction_waits_for_every_stream(gpu):
         pool_c = up(np.full(L * S * N * B * rb, SENTINEL, np.uint8), gpu)
         a, b = torch.cuda.Stream(), torch.cuda.Stream()
         torch.cuda.synchronize()
+        if warm:
+            for st in (a, b):
+                kv.kvm_unpack_layer(c.handle, layout, pool_c, L, 1, [kv.seq(bt, fb, 0)], stream=st)
+                kv.kvm_unpack_layer(c.handle, layout, pool_c, L, 1, [kv.seq(bt, fb, 8)], stream=st)
+            torch.cuda.synchronize()
         c.set_max_workgroups(1)
         kv.kvm_unpack_layer(c.handle, layout, pool_a, L, 0, [kv.seq(bt, fb, T)], stream=a)
         c.set_max_workgroups(0)
