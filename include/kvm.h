@@ -277,7 +277,9 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  * all of a context's unpack and fused calls use one stream, stream order
  * provides that and nothing is recorded per call; the first call on a second
  * stream waits on the host for the device once, and from then on each call
- * records an event that a later replacement waits for on the host.
+ * records an event that a later replacement waits for on the host. Streams
+ * are told apart by handle: synchronize a stream before destroying it if a
+ * context's launches on it may still be running.
  * Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
  * [0, num_layers) or more than 2048 sequences with tokens in one call, and
  * KVM_ECHECK (checks on, kvm_ctx_set_checks). */
