@@ -64,6 +64,7 @@ struct OrderSlot {
     int32_t* order = nullptr;
     int64_t cap = 0;
     hipEvent_t ready = nullptr;         // after the sort kernels
+    bool ready_set = false;             // ready recorded for this sort (several streams seen)
     std::vector<OrderReader> readers;   // per stream; an eviction waits for all
     hipStream_t stream = nullptr;       // where the sort ran
     uint64_t used = 0;
@@ -332,7 +333,7 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     ++c->order_tick;
     for (OrderSlot& o : c->orders) {
         if (o.valid && o.key == key) {
-            if (o.stream != st) {
+            if (o.stream != st && o.ready_set) {
                 hipError_t e = hipStreamWaitEvent(st, o.ready, 0);
                 if (e != hipSuccess) return fail_hip(c, e, "hipStreamWaitEvent");
             }
@@ -345,7 +346,7 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     for (OrderSlot& x : c->orders)
         if (x.used < o->used) o = &x;
     if (o->valid) {  // its sort or launches reading it may still be in flight
-        hipError_t e = hipEventSynchronize(o->ready);
+        hipError_t e = o->ready_set ? hipEventSynchronize(o->ready) : hipSuccess;
         if (e == hipSuccess) e = wait_readers(*o);
         if (e != hipSuccess) return fail_hip(c, e, "hipEventSynchronize");
         o->valid = false;
@@ -391,11 +392,16 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
         return fail_hip(c, e, "hipStreamWaitEvent");
     e = kvm::launch_unpack_order(b, num_blocks, c->d_count, o->order, st);
     if (e != hipSuccess) return fail_hip(c, e, "unpack order launch");
-    if ((e = hipEventRecord(o->ready, st)) != hipSuccess ||
-        (e = hipEventRecord(c->count_done, st)) != hipSuccess)
-        return fail_hip(c, e, "hipEventRecord");
-    c->count_stream = st;
-    c->count_pending = true;
+    // on one stream, stream order covers later readers and the next sort;
+    // the first call on a second stream waits for the device instead
+    o->ready_set = c->order_streams.multi;
+    if (c->order_streams.multi) {
+        if ((e = hipEventRecord(o->ready, st)) != hipSuccess ||
+            (e = hipEventRecord(c->count_done, st)) != hipSuccess)
+            return fail_hip(c, e, "hipEventRecord");
+        c->count_stream = st;
+        c->count_pending = true;
+    }
     o->key = std::move(key);
     o->stream = st;
     o->used = c->order_tick;
