@@ -6,6 +6,8 @@ that switch, under eviction and with slow launches (a one-workgroup budget)
 still reading on another stream. Every record set writes its own pool blocks
 and its own output rows, and repeating a call writes the same bytes, so the
 final state does not depend on how the streams interleave."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,10 @@ from paged_kv_cache_kvm_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("seed", [1, 2, 3])
+SEEDS = int(os.environ.get("KVM_STREAM_SEEDS", "3"))
+
+
+@pytest.mark.parametrize("seed", range(1, SEEDS + 1))
 def test_interleaved_streams(gpu, seed):
     rng = np.random.default_rng(500 + seed)
     L, S, B, rb = 2, 2, 4, 64
