@@ -18,7 +18,11 @@ requests), the small-object batched copy (200000 objects of 256*U{16..512}
 bytes), the 256,000-object restore list, the per-call cost of small calls,
 and the oracle timed on the host cores on one request of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-batch-copy]
+Inputs are seeded: --seed S (default 1002) draws the layer loop from S, the
+restore list from S+1, the MLA loop from S+2 and the small-object list from
+S+3 (the defaults are the workloads' own seeds).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S] [--no-cpu] [--no-batch-copy]
                       [--no-host] [--no-pipeline] [--no-mla]
                       [--no-restore] [--no-small]
 """
@@ -47,6 +51,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=1002,
+                    help="base seed of the synthetic inputs (layer loop S, restore list S+1, "
+                         "MLA loop S+2, small objects S+3)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-batch-copy", action="store_true", help="skip the batched-copy section")
     ap.add_argument("--no-host", action="store_true", help="skip the pinned-host-buffer section")
@@ -90,8 +97,9 @@ def quantile(xs, q):
     return xs[lo] + (xs[hi] - xs[lo]) * (pos - lo)
 
 
-def llama_setup(torch, kv, wl, dev):
-    w = wl.LLAMA8B
+def llama_setup(torch, kv, wl, dev, seed):
+    import dataclasses
+    w = dataclasses.replace(wl.LLAMA8B, seed=seed)
     sh = w.shape
     L, S, B, rb, N = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, w.pool_blocks
     C = sh.c_kv_bytes
@@ -398,8 +406,9 @@ def copy_ceilings(torch, kv, ctx, dev, nbytes=2 << 30, reps=10):
     return torch_copy, stream_copy
 
 
-def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
-    w = wl.SMALL_OBJS
+def batch_copy_section(torch, kv, wl, ctx, dev, seed, reps=10):
+    import dataclasses
+    w = dataclasses.replace(wl.SMALL_OBJS, seed=seed)
     descs_np = wl.small_object_descs(w)
     total = int(descs_np[:, 2].sum())
     log(f"[bench] {w.name}: {len(descs_np)} objects, {total / 1e9:.2f} GB each way")
@@ -429,12 +438,12 @@ def batch_copy_section(torch, kv, wl, ctx, dev, reps=10):
             "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
 
 
-def mla_section(torch, kv, wl, ctx, dev, reps=5):
+def mla_section(torch, kv, wl, ctx, dev, seed, reps=5):
     """The MLA agentic layer loop (64 requests, T_hit ~ U{16384..65536},
     T_miss ~ U{128..1024}, 61 layers of one 576-element bf16 latent, B=64, a
     one-layer slot pool): per layer unpack + merge into a 2-deep complete_layer
     ring, and the same loop with the fused call."""
-    w = wl.mla_agentic()
+    w = wl.mla_agentic(seed)
     sh = w.shape
     L, S, B, rb, C = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, sh.c_kv_bytes
     R = len(w.t_hit)
@@ -548,18 +557,18 @@ def small_call_section(torch, kv, wl, ctx, dev, calls=2000):
             "calls": calls}
 
 
-def restore_section(torch, kv, wl, ctx, dev, reps=10):
+def restore_section(torch, kv, wl, ctx, dev, seed, reps=10):
     """The long-sequence restore list (one 128,000-token sequence of a
     Qwen3-32B-like model, L=64, B=64: 256,000 K/V objects of 128 KiB from
     random staging offsets into their paged slots), as one batched copy and as
     one call per layer (4,000 objects each)."""
-    descs_np, _, pool_bytes = wl.qwen32b_object_descs()
+    descs_np, _, pool_bytes = wl.qwen32b_object_descs(seed)
     n, L = len(descs_np), wl.QWEN32B_SHAPE.layers
     total = int(descs_np[:, 2].sum())
     log(f"[bench] restore: {n} objects of 128 KiB, {total / 1e9:.2f} GB each way")
     u8 = dict(dtype=torch.uint8, device=dev)
     staging = torch.empty(wl.QWEN32B_STAGING, **u8)
-    wl.fill_random_bytes_(staging, 1003, 3)
+    wl.fill_random_bytes_(staging, seed, 3)
     pool = torch.empty(pool_bytes, **u8)
     descs = torch.from_numpy(descs_np.view(__import__("numpy").uint8).reshape(-1)).to(dev)
     per = n // L
@@ -737,7 +746,7 @@ def main():
     kv.load()
     ctx = kv.Context(0)
 
-    s = llama_setup(torch, kv, wl, dev)
+    s = llama_setup(torch, kv, wl, dev, args.seed)
     step_bytes = sum(s["bytes"][k] * s["launches"][k] for k in s["bytes"])
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -788,9 +797,9 @@ def main():
     ceiling, stream_copy = copy_ceilings(torch, kv, ctx, dev)
     for v in ops.values():
         v["pct_of_copy_ceiling"] = round(100 * v["GBps"] / max(ceiling, stream_copy), 1)
-    mla = None if args.no_mla else mla_section(torch, kv, wl, ctx, dev)
-    bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev)
-    restore = None if args.no_restore else restore_section(torch, kv, wl, ctx, dev)
+    mla = None if args.no_mla else mla_section(torch, kv, wl, ctx, dev, args.seed + 2)
+    bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev, args.seed + 3)
+    restore = None if args.no_restore else restore_section(torch, kv, wl, ctx, dev, args.seed + 1)
     small = None if args.no_small else small_call_section(torch, kv, wl, ctx, dev)
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
@@ -803,7 +812,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": workload, "payload": "bf16 ~ N(0,1)", "layers": 32, "h_kv": 8,
                    "head_dim": 128, "block_tokens": 16, "requests": 8, "t_hit": 32768,
-                   "t_miss": 512, "pool_blocks": 24576,
+                   "t_miss": 512, "pool_blocks": 24576, "seed": args.seed,
                    "step": "32 x (unpack_layer + merge_layer) + pack_full",
                    "bytes_per_step": step_bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

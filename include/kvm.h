@@ -161,30 +161,40 @@ typedef struct {
     uint64_t nbytes;
 } kvm_copy_desc;
 
-/* KVM_ABI_VERSION of the built library. */
+/* KVM_ABI_VERSION of the built library. A caller compares it with the
+ * KVM_ABI_VERSION it was compiled against before creating a context. */
 int kvm_version(void);
 
 /* Static text for a status code. Never NULL. */
 const char* kvm_strerror(int status);
 
-/* Create a context on HIP device `device`. It owns a device error counter
- * and the batched copy's scratch (two 64-bit words per 64 copy objects).
+/* Create a context on HIP device `device` (the "initialize engine" step of
+ * the transfer lifecycle in Mooncake Ascend Transports, USE_ASCEND_DIRECT:
+ * initialize, register memory, transfer asynchronously, query completion,
+ * finalize; here a transfer is a call below and its completion is the
+ * caller's stream). It owns a device error counter and the batched copy's
+ * scratch (two 64-bit words per 64 copy objects).
  * *out is set only on KVM_OK. Errors: KVM_EINVAL (out NULL, device < 0),
  * KVM_EHIP (no such device, runtime failure), KVM_ENOMEM. */
 int kvm_create(int device, kvm_ctx** out);
 
-/* Wait for the context's outstanding work, then free it. NULL is a no-op. */
+/* The "finalize" step of the same lifecycle (Mooncake Ascend Transports,
+ * USE_ASCEND_DIRECT): wait for the context's outstanding work, then free it.
+ * NULL is a no-op. */
 void kvm_destroy(kvm_ctx* ctx);
 
 /* Pre-size the batched copy's scratch for up to max_descs copy objects per
- * call, so that later calls allocate nothing. A call with more objects than
+ * call, so that later calls allocate nothing (the lifecycle's "register
+ * memory" step, Mooncake Ascend Transports, USE_ASCEND_DIRECT: resources are
+ * set up once, before the transfers that use them). A call with more objects than
  * the reserve grows the scratch itself (synchronising the device once).
  * max_seqs, the sequences per call, needs no memory and is only range-checked
  * (at most 2^20). Errors: KVM_EINVAL (negative sizes), KVM_ERANGE, KVM_ENOMEM,
  * KVM_EHIP. */
 int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
 
-/* Pre-size the unpack tile-order scratch: every order slot of the context
+/* Pre-size the unpack tile-order scratch, as kvm_ctx_reserve does for the
+ * batched copy (the same "register memory" step): every order slot of the context
  * (16) holds max_tiles entries, and the counting sort serves pools of up to
  * max_pool_blocks blocks. Later kvm_unpack_layer and kvm_unpack_merge_layer
  * calls whose launch batches (128 sequences each) hold at most max_tiles

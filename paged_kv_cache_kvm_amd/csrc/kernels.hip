@@ -71,10 +71,14 @@ template <> struct Unit<1> { typedef uint8_t T; };
 typedef Unit<16>::T V16;
 
 // Streaming cache policy. Every payload byte is read once and written once,
-// so loads are non-temporal, and 16-byte stores carry "sc1 nt" (system-scope,
-// non-temporal): measured on MI355X, this mix moves 3-4 % more copy traffic
-// through HBM than default-policy stores, and more for scattered objects.
-// Narrower units (unaligned edge cases) use default stores.
+// so loads are non-temporal, and 16-byte stores carry "sc1 nt" (on gfx950,
+// sc1 without sc0 is agent (device) scope; system scope would be "sc0 sc1";
+// nt marks the line as streaming): measured on MI355X, this mix moves 3-4 %
+// more copy traffic through HBM than default-policy stores, and more for
+// scattered objects. Stores into pinned host memory (a host-resident Full
+// Block or complete_layer) become visible to the host through the release at
+// the end of the kernel, not through the store's own scope. Narrower units
+// (unaligned edge cases) use default stores.
 template <class V>
 __device__ __forceinline__ V ld(const V* p)
 {
