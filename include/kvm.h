@@ -366,6 +366,28 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
                    uint64_t src_bytes, const kvm_copy_desc* descs, int64_t n_descs,
                    void* stream);
 
+/* The largest n_descs kvm_batch_copy_noalloc accepts (2^26 - 64 objects: 2^20 - 1 groups of 64). */
+#define KVM_NOALLOC_MAX_DESCS ((INT64_C(1) << 26) - 64)
+
+/* For callers that cannot allocate device memory during a call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kvm_batch_copy with its scratch in a static device array of 16 MiB per GPU
+ * (the group sums and bases of the list, 16 bytes per 64 objects), which the
+ * library reserves for the life of the process on every device it runs on.
+ * Same arguments, result and error behaviour as kvm_batch_copy, except:
+ *   - it calls no hipMalloc, hipFree or other allocating routine, records no
+ *     event and never waits on another stream;
+ *   - lists longer than KVM_NOALLOC_MAX_DESCS objects return KVM_ERANGE;
+ *   - every call on one GPU, from any context or stream, shares that GPU's
+ *     array, which keeps the last call's contents: calls that overlap on one
+ *     GPU (on two streams, or from two threads) race and give an unspecified
+ *     result. Order them on one stream, or synchronise between them;
+ *   - the debug checks of kvm_ctx_set_checks are not applied.
+ * The array's address is taken when the context is created (kvm_create). */
+int kvm_batch_copy_noalloc(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes,
+                           const void* src_base, uint64_t src_bytes,
+                           const kvm_copy_desc* descs, int64_t n_descs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

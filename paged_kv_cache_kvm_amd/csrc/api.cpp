@@ -19,6 +19,9 @@ using kvm::SeqRec;
 
 static_assert(sizeof(kvm_copy_desc) == 24, "kvm_copy_desc is 24 bytes");
 static_assert(sizeof(CopyDesc) == sizeof(kvm_copy_desc), "device descriptor mirrors the ABI");
+// the static scratch holds a list's group sums and group bases (2*groups + 1 words)
+static_assert(2 * ((KVM_NOALLOC_MAX_DESCS + 63) / 64) + 1 <= kvm::kStaticScratchWords,
+              "kvm_batch_copy_noalloc's limit fits the static scratch");
 
 namespace {
 
@@ -108,6 +111,7 @@ struct kvm_ctx {
     hipEvent_t count_done = nullptr;
     hipStream_t count_stream = nullptr;
     bool count_pending = false;
+    uint64_t* static_scratch = nullptr;  // this device's static scratch (kvm_batch_copy_noalloc)
     std::string last_error;
 };
 
@@ -626,6 +630,12 @@ int kvm_create(int device, kvm_ctx** out)
         c->copy_done = nullptr;
         rc = KVM_EHIP;
     }
+    // the static scratch's device address, taken once per device with that
+    // device current (the guard above made it current)
+    if (rc == KVM_OK && kvm::static_scratch(device, &c->static_scratch) != hipSuccess) {
+        c->static_scratch = nullptr;
+        rc = KVM_EHIP;
+    }
     if (rc != KVM_OK) {
         kvm_destroy(c);
         return rc;
@@ -973,6 +983,35 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     if (e != hipSuccess) return fail_hip(ctx, e, "hipEventRecord");
     ctx->copy_stream = st;
     ctx->copy_pending = true;
+    return KVM_OK;
+}
+
+int kvm_batch_copy_noalloc(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,
+                           uint64_t src_bytes, const kvm_copy_desc* descs, int64_t n_descs,
+                           void* stream)
+{
+    if (!ctx || n_descs < 0) return KVM_EINVAL;
+    if (n_descs == 0) return KVM_OK;
+    if (!descs || !dst_base || !src_base) return KVM_EINVAL;
+    if (n_descs > KVM_NOALLOC_MAX_DESCS) return KVM_ERANGE;
+    if (!ctx->static_scratch) return KVM_EHIP;
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return KVM_EHIP;
+    // The same kernels as kvm_batch_copy, with the group sums and bases in the
+    // device's static scratch (no allocation, no event, no wait on another
+    // stream: calls that overlap on one device share that scratch and race).
+    const int64_t groups = (n_descs + kvm::kDescGroup - 1) / kvm::kDescGroup;
+    const bool one_group = groups == 1;
+    const int32_t copy_blocks =
+        ctx->max_wgs > 0 ? std::min(ctx->max_wgs, ctx->num_cus * 8) : ctx->num_cus * 8;
+    const int32_t large_blocks = std::min(copy_blocks, ctx->num_cus * 2);
+    uint64_t* sums = ctx->static_scratch;
+    const hipError_t e = kvm::launch_batch_copy(
+        static_cast<char*>(dst_base), dst_bytes, static_cast<const char*>(src_base), src_bytes,
+        reinterpret_cast<const CopyDesc*>(descs), n_descs, one_group ? nullptr : sums,
+        one_group ? nullptr : sums + groups, copy_blocks, large_blocks, ctx->d_err,
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(ctx, e, "batch copy launch");
     return KVM_OK;
 }
 

@@ -38,6 +38,7 @@
 #include "kvm_internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace kvm {
 
@@ -813,6 +814,39 @@ __global__ __launch_bounds__(kBlock) void k_bc_copy(const CopyDesc* __restrict__
         ++kk;
         cur = nxt;
     }
+}
+
+// ---------------------------------------------------- static scratch ---
+// The scratch of kvm_batch_copy_noalloc: one file-scope device array per
+// GPU the library runs on, held until the process ends. Host code never uses
+// the array's name as an address (on the host it is only a stand-in): each
+// device's address is taken once, with that device current, by
+// static_scratch() below, and the kernels receive that address as an
+// ordinary pointer argument.
+__device__ __align__(256) uint64_t scratch[kStaticScratchWords];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(int device, uint64_t** out)
+{
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device) return hipErrorInvalidDevice;  // the caller makes `device` current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = static_cast<uint64_t*>(p);
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
 }
 
 // ------------------------------------------------------------- launches ---

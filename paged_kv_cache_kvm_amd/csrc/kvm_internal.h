@@ -130,6 +130,14 @@ hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* 
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
                         bool wide, int32_t max_wgs, hipStream_t st);
 
+// Size of the static device scratch used by kvm_batch_copy_noalloc, in
+// 64-bit words (16 MiB per device).
+constexpr int64_t kStaticScratchWords = int64_t(2) << 20;
+
+// The address of the static scratch on `device`, which must be the current
+// device; looked up once per device (hipGetSymbolAddress) and kept.
+hipError_t static_scratch(int device, uint64_t** out);
+
 // group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1; a list of at
 // most 64 objects uses neither (both may be null) and makes one launch.
 // copy_blocks workgroups are launched; when the objects average 64 KiB or more

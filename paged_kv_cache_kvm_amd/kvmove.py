@@ -84,7 +84,10 @@ SIGNATURES = {
     "kvm_unpack_merge_layer": ([_P, ctypes.POINTER(kvm_pool_layout), _P, _I32, _I32,
                                 ctypes.POINTER(kvm_layer_seq), _I32, _P], ctypes.c_int),
     "kvm_batch_copy": ([_P, _P, _U64, _P, _U64, _P, _I64, _P], ctypes.c_int),
+    "kvm_batch_copy_noalloc": ([_P, _P, _U64, _P, _U64, _P, _I64, _P], ctypes.c_int),
 }
+
+KVM_NOALLOC_MAX_DESCS = (1 << 26) - 64
 
 _lib = None
 
@@ -251,6 +254,14 @@ def kvm_batch_copy(ctx: int, dst_base, dst_bytes: int, src_base, src_bytes: int,
     st = load().kvm_batch_copy(ctx, _addr(dst_base), dst_bytes, _addr(src_base), src_bytes,
                                _addr(descs), n_descs, _stream(stream))
     _check("kvm_batch_copy", st, ctx)
+
+
+def kvm_batch_copy_noalloc(ctx: int, dst_base, dst_bytes: int, src_base, src_bytes: int, descs,
+                           n_descs: int, stream=None) -> None:
+    """kvm_batch_copy with its scratch in the device's static array (no allocation)."""
+    st = load().kvm_batch_copy_noalloc(ctx, _addr(dst_base), dst_bytes, _addr(src_base), src_bytes,
+                                       _addr(descs), n_descs, _stream(stream))
+    _check("kvm_batch_copy_noalloc", st, ctx)
 
 
 class Context:

@@ -92,3 +92,10 @@ def test_product_code_never_touches_the_oracle():
                 assert "kvm_ref" not in text, f
     for f in os.listdir(os.path.join(PKG, "csrc")):
         assert "kvm_ref" not in open(os.path.join(PKG, "csrc", f)).read()
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define KVM_NOALLOC_MAX_DESCS \(\(INT64_C\(1\) << (\d+)\) - (\d+)\)", text)
+    assert m, "KVM_NOALLOC_MAX_DESCS not found"
+    assert kvmove.KVM_NOALLOC_MAX_DESCS == (1 << int(m.group(1))) - int(m.group(2))

@@ -1,0 +1,100 @@
+"""kvm_batch_copy_noalloc against kvm_batch_copy (GPU, through the C ABI).
+
+The no-alloc entry point keeps its scratch in the device's static array; its
+output must equal the allocating entry point's, byte for byte, and the
+oracle's, on two calls in a row (the second with a smaller list), while the
+context's device memory stays where it was.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import SENTINEL, down, say, up
+from paged_kv_cache_kvm_amd import kvmove as kv
+from paged_kv_cache_kvm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _list(seed, n, arena):
+    """n objects at random non-overlapping places in both arenas: most of
+    them 16-byte friendly (256-byte granules), some with odd offsets and
+    lengths, one empty and one past the end of the source (skipped)."""
+    rng = np.random.default_rng(seed)
+    lens = 256 * rng.integers(1, 9, size=n).astype(np.int64)
+    src = wl.placements(seed, 1, lens, arena)
+    dst = wl.placements(seed, 2, lens, arena)
+    d = np.stack([src, dst, lens], axis=1).astype(np.uint64)
+    odd = rng.choice(n, size=max(1, n // 10), replace=False)
+    d[odd, 0] += rng.integers(0, 16, size=len(odd)).astype(np.uint64)   # source shifted
+    d[odd, 2] -= rng.integers(16, 200, size=len(odd)).astype(np.uint64)  # shorter, any length
+    d[odd[0], 2] = 0                                                     # an empty object
+    bad = d.copy()
+    bad[-1] = [arena - 8, 0, 64]                                         # past the source end
+    return bad
+
+
+def _copy(entry, ctx, src, dst, arena, descs_np, dev):
+    d = up(descs_np.view(np.uint8), dev)
+    lib = kv.load()
+    rc = getattr(lib, entry)(ctx.handle, dst.data_ptr(), arena, src.data_ptr(), arena,
+                            d.data_ptr(), len(descs_np), torch.cuda.current_stream().cuda_stream)
+    assert rc == kv.KVM_OK, (entry, rc, kv.kvm_ctx_last_error(ctx.handle))
+    torch.cuda.synchronize()
+    return down(dst)
+
+
+def test_noalloc_matches_batch_copy_on_two_calls(gpu):
+    arena = 128 << 20
+    ctx = kv.Context(0)
+    try:
+        # more than 65,536 objects takes the three-launch path; the second,
+        # smaller list the one-workgroup metadata path
+        for call, n in enumerate((70000, 3000)):
+            descs = _list(1000 + call, n, arena)
+            say(f"  call {call}: {n} objects in {arena >> 20} MiB arenas")
+            rng = np.random.default_rng(2000 + call)
+            src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+            src = up(src_np, gpu)
+            dst_a = up(np.full(arena, SENTINEL, np.uint8), gpu)
+            dst_b = up(np.full(arena, SENTINEL, np.uint8), gpu)
+            before = ctx.device_bytes()
+            got_b = _copy("kvm_batch_copy_noalloc", ctx, src, dst_b, arena, descs, gpu)
+            assert ctx.device_bytes() == before, "the no-alloc call changed the context's memory"
+            assert ctx.take_device_errors() == 1   # the object past the source end
+            got_a = _copy("kvm_batch_copy", ctx, src, dst_a, arena, descs, gpu)
+            assert ctx.take_device_errors() == 1
+            assert np.array_equal(got_a, got_b), f"call {call}: no-alloc differs from kvm_batch_copy"
+            want = np.full(arena, SENTINEL, np.uint8)
+            oracle.batch_copy(want, src_np, descs[:-1])
+            assert np.array_equal(got_b, want), f"call {call}: no-alloc differs from the oracle"
+    finally:
+        ctx.close()
+
+
+def test_noalloc_short_list_and_limits(gpu):
+    """A one-group list (at most 64 objects) and the length limit."""
+    arena = 1 << 20
+    ctx = kv.Context(0)
+    try:
+        descs = _list(7, 64, arena)[:-1]           # 63 valid objects, one group
+        rng = np.random.default_rng(8)
+        src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+        src = up(src_np, gpu)
+        dst = up(np.full(arena, SENTINEL, np.uint8), gpu)
+        got = _copy("kvm_batch_copy_noalloc", ctx, src, dst, arena, descs, gpu)
+        want = np.full(arena, SENTINEL, np.uint8)
+        oracle.batch_copy(want, src_np, descs)
+        assert np.array_equal(got, want)
+        lib = kv.load()
+        st = torch.cuda.current_stream().cuda_stream
+        rc = lib.kvm_batch_copy_noalloc(ctx.handle, dst.data_ptr(), arena, src.data_ptr(), arena,
+                                        dst.data_ptr(), kv.KVM_NOALLOC_MAX_DESCS + 1, st)
+        assert rc == kv.KVM_ERANGE   # refused before anything is enqueued
+        assert lib.kvm_batch_copy_noalloc(ctx.handle, dst.data_ptr(), arena, src.data_ptr(), arena,
+                                          dst.data_ptr(), 0, st) == kv.KVM_OK
+        assert ctx.take_device_errors() == 0
+    finally:
+        ctx.close()
