@@ -172,8 +172,10 @@ const char* kvm_strerror(int status);
  * the transfer lifecycle in Mooncake Ascend Transports, USE_ASCEND_DIRECT:
  * initialize, register memory, transfer asynchronously, query completion,
  * finalize; here a transfer is a call below and its completion is the
- * caller's stream). It owns a device error counter and the batched copy's
- * scratch (two 64-bit words per 64 copy objects).
+ * caller's stream). It owns a device error counter, the batched copy's
+ * scratch (sized for lists of 65,536 objects; it grows when a call needs
+ * more) and 512 bytes of pinned host memory where the batched copy's kernels
+ * leave each list shape's piece count (see kvm_batch_copy).
  * *out is set only on KVM_OK. Errors: KVM_EINVAL (out NULL, device < 0),
  * KVM_EHIP (no such device, runtime failure), KVM_ENOMEM. */
 int kvm_create(int device, kvm_ctx** out);
@@ -186,8 +188,11 @@ void kvm_destroy(kvm_ctx* ctx);
 /* Pre-size the batched copy's scratch for up to max_descs copy objects per
  * call, so that later calls allocate nothing (the lifecycle's "register
  * memory" step, Mooncake Ascend Transports, USE_ASCEND_DIRECT: resources are
- * set up once, before the transfers that use them). A call with more objects than
- * the reserve grows the scratch itself (synchronising the device once).
+ * set up once, before the transfers that use them): 32 bytes per 64 objects
+ * and 24 bytes per piece record, with room for max_descs pieces (objects of
+ * up to 128 KiB). A call that needs more (more objects, or more pieces: a
+ * call may need up to min(n_descs, dst_bytes / 16 KiB) + dst_bytes / 128 KiB
+ * + 1) grows the scratch itself (synchronising the device once).
  * max_seqs, the sequences per call, needs no memory and is only range-checked
  * (at most 2^20). Errors: KVM_EINVAL (negative sizes), KVM_ERANGE, KVM_ENOMEM,
  * KVM_EHIP. */
@@ -225,8 +230,8 @@ int kvm_ctx_device_bytes(const kvm_ctx* ctx, int64_t* bytes);
  * for pack, unpack and the fused call, and for merge of rows under 2 KiB
  * (up to 4,194,303 workgroups, the most a dispatch of 1024-thread
  * workgroups can count; above that each takes several items); at most 16
- * workgroups per CU for merge of longer rows, and 8 per CU for the batched
- * copy. The destination-order sort that unpack
+ * workgroups per CU for merge of longer rows; for the batched copy one
+ * 1024-thread workgroup per piece (at least 2 per CU). The destination-order sort that unpack
  * runs once per new set of block tables is not bounded (it touches 8 bytes
  * per tile). Applies to calls enqueued after it returns; calls already
  * enqueued keep their grids. Errors: KVM_EINVAL (null ctx, max_workgroups < 0). */
@@ -342,38 +347,51 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
                            int32_t num_layers, int32_t layer, const kvm_layer_seq* seqs,
                            int32_t n, void* stream);
 
-/* Batched copy of many small non-contiguous objects in one launch sequence
+/* Batched copy of many non-contiguous objects in one launch sequence
  * (Tutti "pseudo-code 1": one submission per layer for thousands of objects;
  * Mooncake Ascend Transports, USE_ASCEND: batching non-contiguous 128 KB blocks):
  * for every k < n_descs,
  *     dst_base[dst_off_k .. dst_off_k + nbytes_k) <- src_base[src_off_k .. + nbytes_k)
  * descs is a DEVICE array of n_descs kvm_copy_desc. dst_bytes and src_bytes are
  * the sizes of the two buffers; an object outside its buffer is skipped and
- * counted (kvm_take_device_errors). Zero-length objects are no-ops. The bytes
- * are split evenly over the device's wavefronts (8 workgroups per CU, or 2
- * when the objects average 64 KiB or more and the call moves 1 GiB or more),
- * so a few large objects and many small ones balance alike. A list of at most
- * 64 objects is copied by one launch that uses none of the context's scratch
- * (it allocates nothing and orders itself after no other stream's copy);
- * longer lists first sum and scan their objects' sizes (one more launch, two
- * above 65,536 objects) in the scratch. The first such call on a second
- * stream waits on the host for the device once; from then on a call on
- * another stream than the previous one waits, on the device, for that call. dst_base and
- * src_base may be the same buffer. Errors: KVM_EINVAL (null ctx, null
- * descs/bases with n_descs > 0, n_descs < 0), KVM_ERANGE (n_descs above 2^32),
- * KVM_ENOMEM, KVM_EHIP, KVM_ECHECK (checks on). */
+ * counted (kvm_take_device_errors). Zero-length objects are no-ops. dst_base and
+ * src_base may be the same buffer.
+ * How: objects of at least 16 KiB whose source, destination and length are
+ * multiples of 16 bytes are cut into pieces of at most 128 KiB, one 1024-thread
+ * workgroup each; all other objects are shared evenly by the device's
+ * wavefronts. A list of more than 64 objects first runs a metadata pass (one
+ * launch up to 65,536 objects, three above) that sums, scans and records the
+ * pieces in the context's scratch; a list of at most 64 objects is copied by
+ * one launch that uses no scratch (it allocates nothing and orders itself
+ * after no other stream's copy). The number of pieces is known only on the
+ * device: the metadata pass leaves it in pinned host memory under the call's
+ * list shape (n_descs and the two buffers, address and size), and the next
+ * call of that shape sizes its grid from it without waiting for the device;
+ * the first call of a shape guesses, and then loops over the pieces its grid
+ * does not hold (same result, slower). When the previous call of the shape
+ * found every object one piece, the call runs one workgroup per object with
+ * no metadata pass (no scratch); an object that is not one piece then still
+ * moves, and the shape goes back to the metadata pass at its next call.
+ * The first call with scratch on a second stream waits on the host for the
+ * device once; from then on a call on another stream than the previous one
+ * waits, on the device, for that call.
+ * Errors: KVM_EINVAL (null ctx, null descs/bases with n_descs > 0, n_descs < 0),
+ * KVM_ERANGE (n_descs above 2^32), KVM_ENOMEM, KVM_EHIP, KVM_ECHECK (checks on). */
 int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,
                    uint64_t src_bytes, const kvm_copy_desc* descs, int64_t n_descs,
                    void* stream);
 
-/* The largest n_descs kvm_batch_copy_noalloc accepts (2^26 - 64 objects: 2^20 - 1 groups of 64). */
-#define KVM_NOALLOC_MAX_DESCS ((INT64_C(1) << 26) - 64)
+/* The largest n_descs kvm_batch_copy_noalloc accepts (2^25 - 64 objects: 2^19 - 1 groups of 64). */
+#define KVM_NOALLOC_MAX_DESCS ((INT64_C(1) << 25) - 64)
 
 /* For callers that cannot allocate device memory during a call (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * kvm_batch_copy with its scratch in a static device array of 16 MiB per GPU
- * (the group sums and bases of the list, 16 bytes per 64 objects), which the
- * library reserves for the life of the process on every device it runs on.
+ * (the list's sums and bases, 32 bytes per 64 objects, then its piece records,
+ * 24 bytes each), which the library reserves for the life of the process on
+ * every device it runs on. A list whose piece records might not fit (more
+ * than the array holds after the sums, by the bound given for
+ * kvm_ctx_reserve) sends every object to the wavefront shares instead.
  * Same arguments, result and error behaviour as kvm_batch_copy, except:
  *   - it calls no hipMalloc, hipFree or other allocating routine, records no
  *     event and never waits on another stream;

@@ -19,8 +19,8 @@ using kvm::SeqRec;
 
 static_assert(sizeof(kvm_copy_desc) == 24, "kvm_copy_desc is 24 bytes");
 static_assert(sizeof(CopyDesc) == sizeof(kvm_copy_desc), "device descriptor mirrors the ABI");
-// the static scratch holds a list's group sums and group bases (2*groups + 1 words)
-static_assert(2 * ((KVM_NOALLOC_MAX_DESCS + 63) / 64) + 1 <= kvm::kStaticScratchWords,
+// the static scratch holds a list's group sums and bases (4 words per group + 2)
+static_assert(kvm::copy_group_words(KVM_NOALLOC_MAX_DESCS) <= kvm::kStaticScratchWords,
               "kvm_batch_copy_noalloc's limit fits the static scratch");
 
 namespace {
@@ -74,6 +74,29 @@ struct OrderSlot {
     bool valid = false;
 };
 
+// The shape of a batched-copy list as the host sees it. Calls with equal keys
+// (a per-layer loop, a repeated list) share one measured piece count.
+struct CopyHintKey {
+    int64_t n = -1;
+    uintptr_t dst = 0, src = 0;
+    uint64_t dst_bytes = 0, src_bytes = 0;
+    uint64_t used = 0;
+    bool operator==(const CopyHintKey& o) const
+    {
+        return n == o.n && dst == o.dst && src == o.src && dst_bytes == o.dst_bytes &&
+               src_bytes == o.src_bytes;
+    }
+};
+constexpr int kCopyHints = 64;
+// Piece count assumed for a list shape seen for the first time (each
+// workgroup of the copy then loops over pieces b, b + grid, ...).
+constexpr int64_t kPieceGuess = 16384;
+// Most pieces the allocating entry point keeps records for (192 MiB); a list
+// whose piece bound is larger sends every object to the wavefront shares.
+constexpr int64_t kMaxPieces = int64_t(1) << 23;
+// The largest copy grid: a dispatch counts its work-items in 32 bits.
+constexpr int64_t kMaxCopyGrid = int64_t(0xFFFFFFFFu) / 1024;
+
 struct SingleStream {
     hipStream_t home = nullptr;
     bool seen = false;
@@ -89,8 +112,15 @@ struct kvm_ctx {
     bool checks = false;           // host-side precondition checks before each call
     int64_t device_bytes = 0;      // device memory held by this context
     unsigned long long* d_err = nullptr;
-    uint64_t* d_groups = nullptr;  // group sums, then group bases
-    int64_t group_cap = 0;         // groups the scratch holds
+    uint64_t* d_copy = nullptr;    // batched-copy scratch: group sums and bases, piece records
+    int64_t copy_words = 0;        // 64-bit words it holds
+    // Piece counts measured by earlier copies, per list shape (see copy_grid):
+    // hint_keys on the host, the counts (+ 1; 0 = not yet known) in pinned
+    // host memory the kernels write.
+    CopyHintKey hint_keys[kCopyHints];
+    uint64_t* h_hints = nullptr;   // pinned host, kCopyHints words
+    uint64_t* d_hints = nullptr;   // its device-visible address
+    uint64_t hint_tick = 0;
     // The group scratch is reused by every batch copy: a call on another stream
     // first waits (on the device) for the previous call's kernels.
     hipEvent_t copy_done = nullptr;
@@ -414,20 +444,68 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     return KVM_OK;
 }
 
-int grow_groups(kvm_ctx* c, int64_t groups)
+int grow_copy(kvm_ctx* c, int64_t words)
 {
-    if (groups <= c->group_cap) return KVM_OK;
+    if (words <= c->copy_words) return KVM_OK;
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail_hip(c, e, "hipDeviceSynchronize");
-    if (c->d_groups) dev_free(c, c->d_groups, size_t(2 * c->group_cap + 1));
-    c->group_cap = 0;
-    const int64_t cap = std::max<int64_t>(groups, 1024);
-    if (!dev_alloc(c, &c->d_groups, size_t(2 * cap + 1))) {
-        c->last_error = "hipMalloc: batched-copy group scratch";
+    if (c->d_copy) dev_free(c, c->d_copy, size_t(c->copy_words));
+    c->copy_words = 0;
+    const int64_t cap = std::max<int64_t>(words, 8192);
+    if (!dev_alloc(c, &c->d_copy, size_t(cap))) {
+        c->last_error = "hipMalloc: batched-copy scratch";
         return KVM_ENOMEM;
     }
-    c->group_cap = cap;
+    c->copy_words = cap;
     return KVM_OK;
+}
+
+// Grid of a batched copy: one workgroup per piece of the list's big objects
+// (at least 2 per CU, which the wavefront shares of the other objects need),
+// within the workgroup budget. The piece count is known only on the device;
+// each call's metadata pass writes it into the pinned slot of the call's list
+// shape, and the next call of that shape reads it here without waiting. A
+// count that is stale or not yet written only changes the grid: workgroups
+// past the pieces go straight to their shares, and pieces past the grid are
+// taken in turn by the workgroups there are. When the count says every
+// object of the shape was one piece, the call copies one object per
+// workgroup with no metadata pass (*each).
+int64_t copy_grid(kvm_ctx* c, const CopyHintKey& key, bool use_pieces, uint64_t** hint,
+                  bool* each)
+{
+    *hint = nullptr;
+    *each = false;
+    int64_t np = 0;
+    if (use_pieces) {
+        CopyHintKey* slot = nullptr;
+        for (CopyHintKey& k : c->hint_keys)
+            if (k == key) slot = &k;
+        const int idx = [&] {
+            if (slot) return int(slot - c->hint_keys);
+            int lru = 0;
+            for (int i = 1; i < kCopyHints; ++i)
+                if (c->hint_keys[i].used < c->hint_keys[lru].used) lru = i;
+            return lru;
+        }();
+        if (!slot) {
+            c->hint_keys[idx] = key;
+            reinterpret_cast<volatile uint64_t*>(c->h_hints)[idx] = 0;
+        }
+        c->hint_keys[idx].used = ++c->hint_tick;
+        const uint64_t v = reinterpret_cast<volatile uint64_t*>(c->h_hints)[idx];
+        *hint = c->d_hints + idx;
+        // one workgroup per object needs a grid of every object, so no budget
+        if ((v & kvm::kHintUniform) && key.n > kvm::kDescGroup && key.n <= kMaxCopyGrid &&
+            (c->max_wgs == 0 || c->max_wgs >= key.n)) {
+            *each = true;
+            np = key.n;
+        } else {
+            np = v ? int64_t((v & ~kvm::kHintUniform) - 1) : std::min<int64_t>(key.n, kPieceGuess);
+        }
+    }
+    int64_t grid = *each ? np : std::max<int64_t>(np, 2 * int64_t(c->num_cus));
+    if (c->max_wgs > 0) grid = std::min<int64_t>(grid, c->max_wgs);
+    return std::max<int64_t>(1, std::min(grid, kMaxCopyGrid));
 }
 
 // ------------------------------------------------ precondition checks ---
@@ -625,7 +703,19 @@ int kvm_create(int device, kvm_ctx** out)
         delete c;
         return KVM_EHIP;
     }
-    int rc = grow_groups(c, 1024);
+    int rc = grow_copy(c, kvm::copy_group_words(65536));
+    if (rc == KVM_OK) {
+        void* h = nullptr;
+        if (hipHostMalloc(&h, sizeof(uint64_t) * kCopyHints, hipHostMallocDefault) != hipSuccess) {
+            rc = KVM_ENOMEM;
+        } else {
+            c->h_hints = static_cast<uint64_t*>(h);
+            std::memset(h, 0, sizeof(uint64_t) * kCopyHints);
+            void* d = nullptr;
+            if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess) rc = KVM_EHIP;
+            c->d_hints = static_cast<uint64_t*>(d);
+        }
+    }
     if (rc == KVM_OK && hipEventCreateWithFlags(&c->copy_done, hipEventDisableTiming) != hipSuccess) {
         c->copy_done = nullptr;
         rc = KVM_EHIP;
@@ -651,7 +741,8 @@ void kvm_destroy(kvm_ctx* ctx)
     (void)hipDeviceSynchronize();
     order_release(ctx);
     if (ctx->copy_done) (void)hipEventDestroy(ctx->copy_done);
-    if (ctx->d_groups) dev_free(ctx, ctx->d_groups, size_t(2 * ctx->group_cap + 1));
+    if (ctx->d_copy) dev_free(ctx, ctx->d_copy, size_t(ctx->copy_words));
+    if (ctx->h_hints) (void)hipHostFree(ctx->h_hints);
     dev_free(ctx, ctx->d_err, 1);
     delete ctx;
 }
@@ -662,7 +753,9 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs)
     if (max_seqs > kMaxSeqs || max_descs > kMaxDescs) return KVM_ERANGE;
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
-    return grow_groups(ctx, (max_descs + kvm::kDescGroup - 1) / kvm::kDescGroup);
+    // group sums and bases, and the records of one piece per object (objects
+    // of up to 128 KiB)
+    return grow_copy(ctx, kvm::copy_group_words(max_descs) + 3 * std::min(max_descs, kMaxPieces));
 }
 
 int kvm_ctx_reserve_unpack(kvm_ctx* ctx, int64_t max_tiles, int64_t max_pool_blocks)
@@ -951,34 +1044,47 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
         if (rc != KVM_OK) return rc;
     }
     // A list of one group (at most 64 objects) is copied in one launch that
-    // uses no group scratch: no allocation, and no wait on another stream's
-    // use of the scratch.
+    // uses no scratch: no allocation, and no wait on another stream's use of
+    // the scratch.
     const int64_t groups = (n_descs + kvm::kDescGroup - 1) / kvm::kDescGroup;
     const bool one_group = groups == 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!one_group) {
+    const int64_t bound = kvm::copy_piece_bound(n_descs, dst_bytes);
+    const bool use_pieces = bound <= kMaxPieces;
+    const int64_t piece_cap = use_pieces ? bound : 0;
+    CopyHintKey key;
+    key.n = n_descs;
+    key.dst = uintptr_t(dst_base);
+    key.src = uintptr_t(src_base);
+    key.dst_bytes = dst_bytes;
+    key.src_bytes = src_bytes;
+    kvm::BatchCopyArgs a;
+    a.grid = copy_grid(ctx, key, use_pieces, &a.hint, &a.each);
+    // one group or one workgroup per object: no scratch
+    const bool scratch = !one_group && !a.each;
+    if (scratch) {
         int rc = enter_stream(ctx, &ctx->copy_streams, st);
-        if (rc == KVM_OK) rc = grow_groups(ctx, groups);
+        if (rc == KVM_OK) rc = grow_copy(ctx, kvm::copy_group_words(n_descs) + 3 * piece_cap);
         if (rc != KVM_OK) return rc;
     }
-    // Enough wavefronts to cover every CU several times over, or the
-    // workgroup budget if smaller; each takes an equal share of the bytes.
-    // Lists of large objects use 2 workgroups per CU (within the budget).
-    const int32_t copy_blocks =
-        ctx->max_wgs > 0 ? std::min(ctx->max_wgs, ctx->num_cus * 8) : ctx->num_cus * 8;
-    const int32_t large_blocks = std::min(copy_blocks, ctx->num_cus * 2);
+    a.dst = static_cast<char*>(dst_base);
+    a.dst_bytes = dst_bytes;
+    a.src = static_cast<const char*>(src_base);
+    a.src_bytes = src_bytes;
+    a.descs = reinterpret_cast<const CopyDesc*>(descs);
+    a.n = n_descs;
+    a.scratch = scratch ? ctx->d_copy : nullptr;
+    a.piece_cap = piece_cap;
+    a.use_pieces = use_pieces ? 1u : 0u;
+    a.err = ctx->d_err;
     hipError_t e;
-    if (!one_group && ctx->copy_pending && ctx->copy_stream != st) {
+    if (scratch && ctx->copy_pending && ctx->copy_stream != st) {
         e = hipStreamWaitEvent(st, ctx->copy_done, 0);
         if (e != hipSuccess) return fail_hip(ctx, e, "hipStreamWaitEvent");
     }
-    e = kvm::launch_batch_copy(
-        static_cast<char*>(dst_base), dst_bytes, static_cast<const char*>(src_base), src_bytes,
-        reinterpret_cast<const CopyDesc*>(descs), n_descs, one_group ? nullptr : ctx->d_groups,
-        one_group ? nullptr : ctx->d_groups + ctx->group_cap, copy_blocks, large_blocks,
-        ctx->d_err, st);
+    e = kvm::launch_batch_copy(a, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "batch copy launch");
-    if (one_group || !ctx->copy_streams.multi) return KVM_OK;
+    if (!scratch || !ctx->copy_streams.multi) return KVM_OK;
     e = hipEventRecord(ctx->copy_done, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "hipEventRecord");
     ctx->copy_stream = st;
@@ -997,20 +1103,34 @@ int kvm_batch_copy_noalloc(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, con
     if (!ctx->static_scratch) return KVM_EHIP;
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
-    // The same kernels as kvm_batch_copy, with the group sums and bases in the
-    // device's static scratch (no allocation, no event, no wait on another
-    // stream: calls that overlap on one device share that scratch and race).
+    // The same kernels as kvm_batch_copy, with the group sums and bases and
+    // the piece records in the device's static scratch (no allocation, no
+    // event, no wait on another stream: calls that overlap on one device share
+    // that scratch and race). Piece records that might not fit send every
+    // object to the wavefront shares instead.
     const int64_t groups = (n_descs + kvm::kDescGroup - 1) / kvm::kDescGroup;
-    const bool one_group = groups == 1;
-    const int32_t copy_blocks =
-        ctx->max_wgs > 0 ? std::min(ctx->max_wgs, ctx->num_cus * 8) : ctx->num_cus * 8;
-    const int32_t large_blocks = std::min(copy_blocks, ctx->num_cus * 2);
-    uint64_t* sums = ctx->static_scratch;
-    const hipError_t e = kvm::launch_batch_copy(
-        static_cast<char*>(dst_base), dst_bytes, static_cast<const char*>(src_base), src_bytes,
-        reinterpret_cast<const CopyDesc*>(descs), n_descs, one_group ? nullptr : sums,
-        one_group ? nullptr : sums + groups, copy_blocks, large_blocks, ctx->d_err,
-        static_cast<hipStream_t>(stream));
+    const int64_t free_words = kvm::kStaticScratchWords - kvm::copy_group_words(n_descs);
+    const int64_t bound = kvm::copy_piece_bound(n_descs, dst_bytes);
+    const bool use_pieces = bound <= free_words / 3;
+    CopyHintKey key;
+    key.n = n_descs;
+    key.dst = uintptr_t(dst_base);
+    key.src = uintptr_t(src_base);
+    key.dst_bytes = dst_bytes;
+    key.src_bytes = src_bytes;
+    kvm::BatchCopyArgs a;
+    a.dst = static_cast<char*>(dst_base);
+    a.dst_bytes = dst_bytes;
+    a.src = static_cast<const char*>(src_base);
+    a.src_bytes = src_bytes;
+    a.descs = reinterpret_cast<const CopyDesc*>(descs);
+    a.n = n_descs;
+    a.scratch = groups == 1 ? nullptr : ctx->static_scratch;
+    a.piece_cap = use_pieces ? bound : 0;
+    a.use_pieces = use_pieces ? 1u : 0u;
+    a.grid = copy_grid(ctx, key, use_pieces, &a.hint, &a.each);
+    a.err = ctx->d_err;
+    const hipError_t e = kvm::launch_batch_copy(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(ctx, e, "batch copy launch");
     return KVM_OK;
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace kvm {
 
 // Workgroup size of the batched-copy kernels: four wave64 wavefronts. (The
@@ -130,6 +132,55 @@ hipError_t launch_unpack_order(const SeqBatch& b, int64_t num_blocks, uint32_t* 
 hipError_t launch_merge(int unit, int64_t row_bytes, int32_t rows_per_tile, const MergeBatch& b,
                         bool wide, int32_t max_wgs, hipStream_t st);
 
+// Batched copy: objects of at least kBigObject bytes whose source,
+// destination and length are multiples of 16 bytes are cut into pieces of at
+// most kPieceBytes, one 1024-thread workgroup each; all other objects are
+// copied by wavefronts that share their bytes equally.
+constexpr uint64_t kBigObject = 16 * 1024;
+constexpr uint64_t kPieceBytes = 128 * 1024;
+
+// Set in the count a metadata pass leaves for the host when every object of
+// the list was exactly one piece.
+constexpr uint64_t kHintUniform = uint64_t(1) << 63;
+
+// One piece of a big object: absolute device addresses and its length.
+struct PieceRec {
+    uint64_t src;
+    uint64_t dst;
+    uint64_t nbytes;
+};
+
+// Scratch words a list of n objects needs, without and with its pieces: two
+// sums and two bases per 64-object group (plus the two totals), then one
+// three-word record per piece. A list of one group needs none.
+constexpr int64_t copy_group_words(int64_t n) { return 4 * ((n + kDescGroup - 1) / kDescGroup) + 2; }
+
+// The most pieces a list can hold when its destinations are disjoint, as they
+// must be: each big object is at least kBigObject bytes inside dst_bytes, and
+// its pieces are one more than its bytes / kPieceBytes at most.
+inline int64_t copy_piece_bound(int64_t n, uint64_t dst_bytes)
+{
+    const uint64_t objs = std::min<uint64_t>(uint64_t(n), dst_bytes / kBigObject);
+    return int64_t(objs + dst_bytes / kPieceBytes + 1);
+}
+
+struct BatchCopyArgs {
+    char* dst;
+    uint64_t dst_bytes;
+    const char* src;
+    uint64_t src_bytes;
+    const CopyDesc* descs;
+    int64_t n;
+    uint64_t* scratch;     // copy_group_words(n) + 3 * piece_cap words; unused for one group
+    int64_t piece_cap;     // piece records the scratch holds
+    uint32_t use_pieces;   // 0: every object goes to the wavefront shares
+    int64_t grid;          // 1024-thread workgroups of the copy launch
+    bool each;             // one workgroup per object, no metadata launch (k_bc_each)
+    uint64_t* hint;        // receives the list's piece count + 1 and kHintUniform
+                           // (device-visible), or null
+    unsigned long long* err;
+};
+
 // Size of the static device scratch used by kvm_batch_copy_noalloc, in
 // 64-bit words (16 MiB per device).
 constexpr int64_t kStaticScratchWords = int64_t(2) << 20;
@@ -138,13 +189,10 @@ constexpr int64_t kStaticScratchWords = int64_t(2) << 20;
 // device; looked up once per device (hipGetSymbolAddress) and kept.
 hipError_t static_scratch(int device, uint64_t** out);
 
-// group_sum needs ceil(n/64) entries, group_base ceil(n/64)+1; a list of at
-// most 64 objects uses neither (both may be null) and makes one launch.
-// copy_blocks workgroups are launched; when the objects average 64 KiB or more
-// and total 1 GiB or more, only the first large_blocks of them copy.
-hipError_t launch_batch_copy(char* dst, uint64_t dst_bytes, const char* src, uint64_t src_bytes,
-                             const CopyDesc* descs, int64_t n, uint64_t* group_sum,
-                             uint64_t* group_base, int32_t copy_blocks, int32_t large_blocks,
-                             unsigned long long* err, hipStream_t st);
+// Metadata launches (none for a list of one group), then the copy launch of
+// a.grid workgroups: workgroup b copies pieces b, b + grid, ..., then its
+// share of the other objects. With a.each: one launch, workgroup b copying
+// objects b, b + grid, ... whole.
+hipError_t launch_batch_copy(const BatchCopyArgs& a, hipStream_t st);
 
 }  // namespace kvm

@@ -87,7 +87,7 @@ SIGNATURES = {
     "kvm_batch_copy_noalloc": ([_P, _P, _U64, _P, _U64, _P, _I64, _P], ctypes.c_int),
 }
 
-KVM_NOALLOC_MAX_DESCS = (1 << 26) - 64
+KVM_NOALLOC_MAX_DESCS = (1 << 25) - 64
 
 _lib = None
 

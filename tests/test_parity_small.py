@@ -529,3 +529,37 @@ def test_order_eviction_waits_for_every_stream(gpu, warm):
         assert c.take_device_errors() == 0
     finally:
         c.close()
+
+
+def test_batch_copy_list_shape_changes(ctx, gpu):
+    """The grid of a batched copy comes from the piece count the previous call
+    of the same list shape (object count and buffers) measured; a shape whose
+    objects were all one piece is next copied one workgroup per object with
+    no metadata pass. Every call must equal the oracle whatever the previous
+    call saw: the same buffers and object count with a uniform list (twice,
+    the second taking one workgroup per object), then a changed list (short,
+    misaligned and multi-piece objects) under the same shape, then again."""
+    rng = np.random.default_rng(77)
+    arena = 64 << 20
+    n = 300
+    src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+    src = up(src_np, gpu)
+    dst = up(np.full(arena, SENTINEL, np.uint8), gpu)
+    want = np.full(arena, SENTINEL, np.uint8)
+    uniform = np.full(n, 128 << 10, np.int64)
+    changed = 256 * rng.integers(1, 2048, size=n).astype(np.int64)    # up to 512 KiB
+    changed[::7] = rng.integers(1, 5000, size=len(changed[::7]))       # short, any length
+    for call, lens in enumerate((uniform, uniform, changed, changed, uniform)):
+        slots = -(-lens // 256) * 256                                  # whole granules
+        d = np.stack([wl.placements(300 + call, 1, slots, arena),
+                      wl.placements(300 + call, 2, slots, arena), lens], axis=1).astype(np.uint64)
+        if call >= 2:
+            d[1::5, 0] += 3                                            # source misaligned
+            d[1::5, 2] = np.minimum(d[1::5, 2], 1000)
+        say(f"  call {call}: {n} objects, {int(d[:, 2].sum())} bytes")
+        dd = up(d.view(np.uint8), gpu)
+        kv.kvm_batch_copy(ctx.handle, dst, arena, src, arena, dd, n)
+        torch.cuda.synchronize()                                       # the count comes back
+        oracle.batch_copy(want, src_np, d)
+        assert np.array_equal(down(dst), want), f"call {call} differs"
+    assert ctx.take_device_errors() == 0
