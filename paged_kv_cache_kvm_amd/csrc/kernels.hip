@@ -25,12 +25,14 @@
 //                       of 2 KiB and more the grid is capped (16 workgroups
 //                       per CU) and each workgroup walks tiles i, i + grid,
 //                       ...; shorter rows take one workgroup per tile.
-//   k_bc_*              batched copy: per-group byte sums (64 objects per
-//                       wavefront), one exclusive scan (one workgroup does
-//                       both for lists of up to 1,024 groups), then a fixed
-//                       grid in which every wavefront copies an equal share
-//                       of the total bytes, walking the objects its share
-//                       covers.
+//   k_bc_*              batched copy: objects of 16 KiB and more (16-byte
+//                       aligned) in pieces of up to 128 KiB, one workgroup
+//                       per piece; every other object in equal wavefront
+//                       shares of their bytes. Per-group sums, their scan
+//                       and the piece records come first (one workgroup for
+//                       lists of up to 1,024 groups, none for one group);
+//                       a list whose objects were all one piece last time
+//                       is copied one workgroup per object (k_bc_each).
 //
 // Page notation (DualPath KV Loading, key-objects table; Tutti reading notes,
 // prerequisites 3 and 5): T tokens, L layers, C_KV = sides * row_bytes per
