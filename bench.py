@@ -12,11 +12,13 @@ Also reported: each op's average launch time from HIP events on the launch
 stream, the roofline of the dominant kernel, the same step with unpack and
 merge fused per layer (kvm_unpack_merge_layer), the host tier (a pinned host
 Full Block / complete_layer over PCIe), the layerwise overlap of the moves
-with a stand-in compute stream under workgroup budgets, two device copy
-ceilings, the MLA agentic layer loop (61 layers, 576-element latent, 64
-requests), the small-object batched copy (200000 objects of 256*U{16..512}
-bytes), the 256,000-object restore list, the per-call cost of small calls,
-and the oracle timed on the host cores on one request of the same workload.
+with a stand-in compute stream under workgroup budgets, two plain device
+copies (reference rates), the MLA agentic layer loop (61 layers, 576-element
+latent, 64 requests), the small-object batched copy (200000 objects of
+256*U{16..512} bytes), the 256,000-object restore list, the per-call cost of
+small calls, and the oracle timed on the host cores on one request of the
+same workload. The layer loop, the MLA loop, the small-object copy and the
+restore list each carry a roofline entry for their dominant kernel.
 
 Inputs are seeded: --seed S (default 1002) draws the layer loop from S, the
 restore list from S+1, the MLA loop from S+2 and the small-object list from
@@ -170,7 +172,7 @@ def llama_fused_step(kv, ctx, s):
     kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, s["pack_seqs"])
 
 
-def fused_section(torch, kv, ctx, s, steps, warmup, step_bytes, ms_separate):
+def fused_section(torch, kv, ctx, s, steps, warmup, ms_separate):
     """The same step with unpack_layer + merge_layer fused per layer."""
     for _ in range(warmup):
         llama_fused_step(kv, ctx, s)
@@ -188,9 +190,13 @@ def fused_section(torch, kv, ctx, s, steps, warmup, step_bytes, ms_separate):
     torch.cuda.synchronize()
     per = ev.mean_ms("fused") / L
     gbs = s["bytes_fused"] / (per * 1e6)
+    # the fused step's own algorithmic bytes: it reads each hit row once
+    fused_step_bytes = L * s["bytes_fused"] + s["bytes"]["pack_full"]
     return {"step": "32 x unpack_merge_layer + pack_full", "ms_per_step": round(ms, 3),
             "speedup_vs_separate": round(ms_separate / ms, 3),
-            "effective_GBps": round(step_bytes / (ms * 1e6), 1),
+            "bytes_per_step": fused_step_bytes,
+            "GBps": round(fused_step_bytes / (ms * 1e6), 1),
+            "pct_hbm_peak": round(100 * fused_step_bytes / (ms * 1e6) / HBM_PEAK_GBS, 2),
             "unpack_merge_layer": {"bytes_per_launch": s["bytes_fused"],
                                    "ms_per_launch": round(per, 4), "GBps": round(gbs, 1),
                                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}}
@@ -379,10 +385,10 @@ def pipeline_section(torch, kv, ctx, s, reps=3, d_model=4096, d_ff=14336):
             "overlapped_by_workgroup_budget": over}
 
 
-def copy_ceilings(torch, kv, ctx, dev, nbytes=2 << 30, reps=10):
+def plain_copies(torch, kv, ctx, dev, nbytes=2 << 30, reps=10):
     """Two device-to-device copies of nbytes, read+write GB/s: torch's copy
-    (the runtime's blit kernel), and a plain 16-byte streaming copy through
-    this library (kvm_batch_copy of one nbytes object)."""
+    (the runtime's blit kernel), and this library's batched copy of one
+    nbytes object."""
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     a.fill_(1)
@@ -435,7 +441,10 @@ def batch_copy_section(torch, kv, wl, ctx, dev, seed, reps=10):
             "ms_per_call": round(ms, 4), "ms_p10_p50_p90": spread, "repetitions": reps,
             "GBps": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-            "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0)}
+            "descriptors_per_s": round(len(descs_np) / (ms * 1e-3), 0),
+            "roofline": roofline("k_bc_copy", "batch_copy (200000 small objects)", 2 * total, ms,
+                                 "one call: HIP events around its metadata launches (k_bc_sums, "
+                                 "k_bc_scan2, k_bc_map) and its k_bc_copy launch")}
 
 
 def mla_section(torch, kv, wl, ctx, dev, seed, reps=5):
@@ -509,6 +518,33 @@ def mla_section(torch, kv, wl, ctx, dev, seed, reps=5):
                      "repetitions": reps, "bytes_per_loop": nbytes,
                      "GBps": round(nbytes / (ms * 1e6), 1),
                      "pct_hbm_peak": round(100 * nbytes / (ms * 1e6) / HBM_PEAK_GBS, 2)}
+    # each op of the separate loop alone (its 61 launches back to back), for
+    # per-launch times and the dominant kernel's roofline
+    per_op = {"unpack_layer": ("k_unpack", 2 * th * C,
+                               lambda: [kv.kvm_unpack_layer(ctx.handle, layout, slot, L, l, seqs)
+                                        for l in range(L)]),
+              "merge_layer": ("k_merge", 2 * ta * C,
+                              lambda: [kv.kvm_merge_layer(ctx.handle, C, merge_l[l])
+                                       for l in range(L)])}
+    for name, (_, _, fn) in per_op.items():
+        for _ in range(reps):
+            ev.around(name, fn)
+    torch.cuda.synchronize()
+    ops = {}
+    for name, (kernel, nbytes, _) in per_op.items():
+        per_launch = [t / L for t in ev.all_ms(name)]
+        ms = statistics.fmean(per_launch)
+        ops[name] = {"kernel": kernel, "bytes_per_launch": nbytes, "ms_per_launch": round(ms, 4),
+                     "ms_per_launch_p10_p50_p90": [round(quantile(per_launch, q), 4)
+                                                   for q in (0.1, 0.5, 0.9)],
+                     "GBps": round(nbytes / (ms * 1e6), 1),
+                     "pct_hbm_peak": round(100 * nbytes / (ms * 1e6) / HBM_PEAK_GBS, 2)}
+    out["ops"] = ops
+    dom = max(ops, key=lambda k: ops[k]["ms_per_launch"])
+    out["roofline"] = roofline(ops[dom]["kernel"], f"mla {dom}", ops[dom]["bytes_per_launch"],
+                               ops[dom]["ms_per_launch"],
+                               f"one launch: HIP events around the op's {L} launches back to "
+                               f"back, divided by {L}")
     assert ctx.take_device_errors() == 0
     del fbs, misses, slot, rings, bts
     torch.cuda.empty_cache()
@@ -549,12 +585,33 @@ def small_call_section(torch, kv, wl, ctx, dev, calls=2000):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e6 / calls
 
+    import ctypes
+    lib = kv.load()
+    arr = kv.records(seqs)
+    lay = ctypes.byref(layout)
+    st = torch.cuda.current_stream().cuda_stream
+    pool_p, src_p, dst_p, descs_p = pool.data_ptr(), src.data_ptr(), dst.data_ptr(), descs.data_ptr()
     return {"unpack_layer_tiny_us": round(per_call(
                 lambda: kv.kvm_unpack_layer(ctx.handle, layout, pool, L, 1, seqs)), 2),
+            "unpack_layer_tiny_records_us": round(per_call(
+                lambda: kv.kvm_unpack_layer(ctx.handle, layout, pool, L, 1, arr)), 2),
+            "unpack_layer_tiny_c_us": round(per_call(
+                lambda: lib.kvm_unpack_layer(ctx.handle, lay, pool_p, L, 1, arr, 1, st)), 2),
+            "pack_full_tiny_c_us": round(per_call(
+                lambda: lib.kvm_pack_full(ctx.handle, lay, pool_p, L, arr, 1, st)), 2),
             "batch_copy_64x4KiB_us": round(per_call(
                 lambda: kv.kvm_batch_copy(ctx.handle, dst, 1 << 22, src, 1 << 22, descs, 64)), 2),
+            "batch_copy_64x4KiB_c_us": round(per_call(
+                lambda: lib.kvm_batch_copy(ctx.handle, dst_p, 1 << 22, src_p, 1 << 22, descs_p, 64,
+                                           st)), 2),
             "torch_copy_4KiB_us": round(per_call(lambda: b.copy_(a)), 2),
-            "calls": calls}
+            "ctypes_call_us": round(per_call(lambda: lib.kvm_version()), 2),
+            "calls": calls,
+            "note": "host clock per call, back to back, no sync between calls; *_us through "
+                    "the Python binding with a list of records, *_records_us with a reused "
+                    "records() array, *_c_us straight through ctypes with every argument "
+                    "prepared once (the C entry point's own cost plus ctypes_call_us, a "
+                    "call of kvm_version)"}
 
 
 def restore_section(torch, kv, wl, ctx, dev, seed, reps=10):
@@ -583,7 +640,7 @@ def restore_section(torch, kv, wl, ctx, dev, seed, reps=10):
                               descs.data_ptr() + l * per * 24, per)
 
     out = {"workload": f"restore list: {n} objects x 128 KiB (L={L}, 2000 blocks, K and V)",
-           "bytes_rw": 2 * total}
+           "bytes_rw": 2 * total, "objects_per_layer_call": per}
     ev = Events(torch)
     for name, fn in (("one_call", one_call), ("per_layer_calls", per_layer)):
         for _ in range(2):
@@ -600,6 +657,11 @@ def restore_section(torch, kv, wl, ctx, dev, seed, reps=10):
                      "repetitions": reps, "GBps": round(gbs, 1),
                      "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                      "descriptors_per_s": round(n / (ms * 1e-3), 0)}
+    # every object is one 128 KiB piece, so after the first call of each list
+    # shape a call is a single k_bc_each launch (one workgroup per object)
+    out["roofline"] = roofline("k_bc_each", "restore list, one call", 2 * total,
+                               out["one_call"]["ms"],
+                               "one call: HIP events around its single k_bc_each launch")
     assert ctx.take_device_errors() == 0
     del staging, pool, descs
     torch.cuda.empty_cache()
@@ -710,26 +772,56 @@ def cpu_baseline(wl, reps=12, host_threads=16):
                                    f"block-aligned token ranges"}}
 
 
-PROFILE = os.path.join(ROOT, "profiles", "llama8b_layer_loop_hbm_traffic.md")
-KERNEL_SOURCES = ("paged_kv_cache_kvm_amd/csrc/kernels.hip", "paged_kv_cache_kvm_amd/csrc/kvm_internal.h")
+PROFILES = os.path.join(ROOT, "profiles")
+# The sources that decide what a launch moves and how: the kernels, and the
+# host code that picks their tiles and grids.
+KERNEL_SOURCES = ("paged_kv_cache_kvm_amd/csrc/kernels.hip",
+                  "paged_kv_cache_kvm_amd/csrc/kvm_internal.h",
+                  "paged_kv_cache_kvm_amd/csrc/api.cpp")
 
 
-def measured_traffic(op):
-    """HBM bytes per launch of `op`'s kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when that summary was taken on
-    other kernel sources than the ones built now."""
+def kernel_source_sha256():
     import hashlib
-    try:
-        line = next(l for l in open(PROFILE) if l.startswith("traffic-json: "))
-    except (OSError, StopIteration):
-        return None
-    rec = json.loads(line[len("traffic-json: "):])
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, f), "rb").read())
-    if rec.get("kernel_source_sha256") != h.hexdigest():
+    return h.hexdigest()
+
+
+def measured_traffic(op):
+    """HBM bytes (read + write) per launch of `op`'s kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summaries under profiles/ (their
+    "traffic-json:" lines), or None when no summary taken on the sources built
+    now has it."""
+    want = kernel_source_sha256()
+    try:
+        names = sorted(os.listdir(PROFILES))
+    except OSError:
         return None
-    return rec["bytes_per_launch"].get(op)
+    for name in names:
+        try:
+            lines = open(os.path.join(PROFILES, name)).read().splitlines()
+        except OSError:
+            continue
+        for line in lines:
+            if not line.startswith("traffic-json: "):
+                continue
+            rec = json.loads(line[len("traffic-json: "):])
+            if rec.get("kernel_source_sha256") == want and op in rec.get("bytes_per_launch", {}):
+                return rec["bytes_per_launch"][op]
+    return None
+
+
+def roofline(kernel, op, bytes_per_launch, ms_per_launch, timed):
+    """The HBM roofline entry of one kernel: algorithmic bytes per launch over
+    its launch time (HIP events on the launch stream; `timed` says what the
+    events bracket), against the 8 TB/s peak, with the measured traffic when a
+    current profile has it."""
+    gbs = bytes_per_launch / (ms_per_launch * 1e6)
+    return {"bound": "hbm", "kernel": kernel, "op": op, "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(op), "algorithmic_bytes_per_launch": bytes_per_launch,
+            "ms_per_launch": round(ms_per_launch, 4), "timed": timed}
 
 
 def main():
@@ -786,17 +878,26 @@ def main():
                      "repetitions": len(per_launch),
                      "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
     dom = max(ops, key=lambda k: ops[k]["ms_per_launch"] * ops[k]["launches_per_step"])
-    fused = fused_section(torch, kv, ctx, s, args.steps, args.warmup, step_bytes, ms_step)
+    fused = fused_section(torch, kv, ctx, s, args.steps, args.warmup, ms_step)
     host = None if args.no_host else host_tier_section(torch, kv, ctx, s)
-    pipe = None if args.no_pipeline else pipeline_section(torch, kv, ctx, s)
+    pipe = None
+    if not args.no_pipeline:
+        # its own context: it uses two streams, and a context that has seen a
+        # second stream records an event per call from then on
+        pctx = kv.Context(0)
+        try:
+            pipe = pipeline_section(torch, kv, pctx, s)
+            assert pctx.take_device_errors() == 0
+        finally:
+            pctx.close()
     assert ctx.take_device_errors() == 0
     workload = s["w"].name
     del s
     torch.cuda.empty_cache()
 
-    ceiling, stream_copy = copy_ceilings(torch, kv, ctx, dev)
-    for v in ops.values():
-        v["pct_of_copy_ceiling"] = round(100 * v["GBps"] / max(ceiling, stream_copy), 1)
+    # Plain copies, for reference only: pack and the fused kernel move more than
+    # either, so neither bounds the ops and no op is reported as a share of them.
+    torch_copy, stream_copy = plain_copies(torch, kv, ctx, dev)
     mla = None if args.no_mla else mla_section(torch, kv, wl, ctx, dev, args.seed + 2)
     bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev, args.seed + 3)
     restore = None if args.no_restore else restore_section(torch, kv, wl, ctx, dev, args.seed + 1)
@@ -817,16 +918,16 @@ def main():
                    "bytes_per_step": step_bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "ops": ops,
-        "roofline": {"bound": "hbm", "kernel": kernel, "op": dom,
-                     "achieved": ops[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ops[dom]["GBps"] / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(dom),
-                     "algorithmic_bytes_per_launch": ops[dom]["bytes_per_launch"]},
+        "roofline": roofline(kernel, dom, ops[dom]["bytes_per_launch"], ops[dom]["ms_per_launch"],
+                             "one launch: HIP events around the op's 32 launches (1 for "
+                             "pack_full) back to back, divided by their count"),
         "fused_layer_loop": fused,
         "host_tier": host,
         "pipeline": pipe,
-        "copy_ceiling_GBps": round(ceiling, 1),
-        "stream_copy_GBps": round(stream_copy, 1),
+        "plain_copy_2GiB_GBps": {"torch_copy": round(torch_copy, 1),
+                                 "kvm_batch_copy_one_object": round(stream_copy, 1),
+                                 "note": "reference rates of a plain device copy, not a "
+                                         "ceiling: pack and the fused kernel move more"},
         "mla_layer_loop": mla,
         "batch_copy": bc,
         "batch_copy_restore": restore,

@@ -57,8 +57,20 @@
  *     object outside its buffer is skipped (its destination is left as it was)
  *     and counted; kvm_take_device_errors() returns the count.
  *   - One context per host thread; calls on one context are not thread-safe.
- *     One context may be used on several streams: calls wait (on the device)
- *     for the context's own scratch where two streams share it.
+ *     One context may be used on several streams: the calls order their use
+ *     of the context's scratch across streams themselves (see kvm_unpack_layer
+ *     and kvm_batch_copy).
+ *   - Waits. No pack, unpack, merge, fused or batched-copy call waits for the
+ *     whole device. Where one would need a buffer that launches already
+ *     enqueued may still read (its scratch grows; a second stream appears),
+ *     it takes a new buffer and keeps the old one allocated until the next
+ *     call that synchronises the device anyway: kvm_ctx_reserve (when it
+ *     resizes or has such buffers to free), kvm_ctx_reserve_unpack,
+ *     kvm_take_device_errors and kvm_destroy, the only calls that do. The
+ *     host waits that remain are on events the library itself recorded, and
+ *     only once a context has seen two streams (a replaced tile order waits
+ *     for the launches that read it), plus kvm_ctx_set_checks' debug mode,
+ *     which synchronises the call's own stream.
  *   - HIP graph capture of these calls is not supported: a captured unpack or
  *     fused launch refers to the context's cached tile order, which a later
  *     call with other block tables may overwrite before the graph replays.
@@ -192,7 +204,10 @@ void kvm_destroy(kvm_ctx* ctx);
  * and 24 bytes per piece record, with room for max_descs pieces (objects of
  * up to 128 KiB). A call that needs more (more objects, or more pieces: a
  * call may need up to min(n_descs, dst_bytes / 16 KiB) + dst_bytes / 128 KiB
- * + 1) grows the scratch itself (synchronising the device once).
+ * + 1) grows the scratch itself, to at least twice its size, without
+ * waiting: the old buffer stays allocated until the next device
+ * synchronisation below. This call synchronises the device when it resizes
+ * the scratch or has such buffers to free, and frees them.
  * max_seqs, the sequences per call, needs no memory and is only range-checked
  * (at most 2^20). Errors: KVM_EINVAL (negative sizes), KVM_ERANGE, KVM_ENOMEM,
  * KVM_EHIP. */
@@ -204,17 +219,19 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs);
  * max_pool_blocks blocks. Later kvm_unpack_layer and kvm_unpack_merge_layer
  * calls whose launch batches (128 sequences each) hold at most max_tiles
  * block-table entries, on pools of at most max_pool_blocks blocks, allocate
- * no device memory. With kvm_ctx_reserve for the batched copy this gives an
- * allocation-free steady state. Synchronises the device and drops cached
- * orders that it resizes. Uses 64 * max_tiles + 8 * max_pool_blocks bytes
+ * no device memory (on one stream: the first call on a second stream takes
+ * fresh order scratch, see kvm_unpack_layer). With kvm_ctx_reserve for the
+ * batched copy this gives an allocation-free steady state. Synchronises the
+ * device, frees replaced scratch and drops cached orders that it resizes. Uses 64 * max_tiles + 8 * max_pool_blocks bytes
  * (plus a small constant). Errors: KVM_EINVAL (null ctx, negative sizes),
  * KVM_ERANGE (max_tiles above 2^31 - 1, max_pool_blocks above 2^31),
  * KVM_ENOMEM, KVM_EHIP. */
 int kvm_ctx_reserve_unpack(kvm_ctx* ctx, int64_t max_tiles, int64_t max_pool_blocks);
 
 /* Device memory the context holds right now, in bytes: its error counter,
- * the batched-copy scratch and the unpack order scratch. It changes only
- * when a call (or a reserve) grows or frees that scratch. Errors: KVM_EINVAL
+ * the batched-copy scratch, the unpack order scratch, and scratch set aside
+ * until the next device synchronisation (see the waits convention above). It
+ * changes only when a call grows, sets aside or frees that scratch. Errors: KVM_EINVAL
  * (null ctx or bytes). */
 int kvm_ctx_device_bytes(const kvm_ctx* ctx, int64_t* bytes);
 
@@ -290,11 +307,14 @@ int kvm_pack_full(kvm_ctx* ctx, const kvm_pool_layout* layout, const void* pool,
  * has tiles). The context keeps 16 such orders; a new record set beyond that
  * replaces the least recently used one, after every launch that read it. While
  * all of a context's unpack and fused calls use one stream, stream order
- * provides that and nothing is recorded per call; the first call on a second
- * stream waits on the host for the device once, and from then on each call
- * records an event that a later replacement waits for on the host. Streams
- * are told apart by handle: synchronize a stream before destroying it if a
- * context's launches on it may still be running.
+ * provides that and nothing is recorded per call. The launches on that first
+ * stream leave no events, so the first call on a second stream does not wait
+ * for them: it sets every cached order and the sort's counters aside (they
+ * stay allocated until the next device synchronisation, see the waits
+ * convention above) and sorts into new ones, which it allocates. From then on
+ * each call records an event that a later replacement waits for on the host.
+ * Streams are told apart by handle: synchronize a stream before destroying it
+ * if a context's launches on it may still be running.
  * Errors: as kvm_pack_full, plus KVM_ERANGE for layer outside
  * [0, num_layers) or more than 2048 sequences with tokens in one call, and
  * KVM_ECHECK (checks on, kvm_ctx_set_checks). */
@@ -372,9 +392,12 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
  * found every object one piece, the call runs one workgroup per object with
  * no metadata pass (no scratch); an object that is not one piece then still
  * moves, and the shape goes back to the metadata pass at its next call.
- * The first call with scratch on a second stream waits on the host for the
- * device once; from then on a call on another stream than the previous one
- * waits, on the device, for that call.
+ * The first call with scratch on a second stream does not wait for the first
+ * stream's copies (they left no events): it sets the scratch aside (allocated
+ * until the next device synchronisation, see the waits convention above) and
+ * takes a new one. From then on each call with scratch records an event, and
+ * a call on another stream than the previous one waits, on the device, for
+ * that call.
  * Errors: KVM_EINVAL (null ctx, null descs/bases with n_descs > 0, n_descs < 0),
  * KVM_ERANGE (n_descs above 2^32), KVM_ENOMEM, KVM_EHIP, KVM_ECHECK (checks on). */
 int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void* src_base,

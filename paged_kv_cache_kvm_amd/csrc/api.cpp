@@ -63,6 +63,7 @@ struct OrderReader {
 constexpr size_t kOrderReaders = 8;  // streams tracked per slot
 
 struct OrderSlot {
+    uint64_t hash = 0;                  // of key (see order_hash)
     std::vector<char> key;
     int32_t* order = nullptr;
     int64_t cap = 0;
@@ -96,6 +97,34 @@ constexpr int64_t kPieceGuess = 16384;
 constexpr int64_t kMaxPieces = int64_t(1) << 23;
 // The largest copy grid: a dispatch counts its work-items in 32 bits.
 constexpr int64_t kMaxCopyGrid = int64_t(0xFFFFFFFFu) / 1024;
+
+// Launch batches of one call, kept in the context and reused: once they have
+// grown to a call's size, the call allocates no host memory. add() starts an
+// empty batch (n = 0, tile0[0] = 0); records past n are stale and never read.
+template <class B>
+class PlanVec {
+  public:
+    void clear() { n_ = 0; }
+    B& add()
+    {
+        if (n_ == v_.size()) v_.emplace_back();
+        B& b = v_[n_++];
+        b.n = 0;
+        b.tile0[0] = 0;
+        return b;
+    }
+    bool empty() const { return n_ == 0; }
+    size_t size() const { return n_; }
+    B& back() { return v_[n_ - 1]; }
+    B& operator[](size_t i) { return v_[i]; }
+    const B& operator[](size_t i) const { return v_[i]; }
+    const B* begin() const { return v_.data(); }
+    const B* end() const { return v_.data() + n_; }
+
+  private:
+    std::vector<B> v_;
+    size_t n_ = 0;
+};
 
 struct SingleStream {
     hipStream_t home = nullptr;
@@ -142,6 +171,17 @@ struct kvm_ctx {
     hipStream_t count_stream = nullptr;
     bool count_pending = false;
     uint64_t* static_scratch = nullptr;  // this device's static scratch (kvm_batch_copy_noalloc)
+    // Scratch that launches may still read when the library replaces it (a
+    // grown buffer; the scratch of the first stream when a second one comes):
+    // kept, and counted in device_bytes, until the next call that
+    // synchronises the device anyway (kvm_ctx_reserve, kvm_ctx_reserve_unpack,
+    // kvm_take_device_errors, kvm_destroy), so that no move call waits for
+    // the whole device.
+    std::vector<std::pair<void*, size_t>> retired;  // pointer, bytes
+    PlanVec<kvm::SeqBatch> seq_plan;       // pack and unpack
+    PlanVec<kvm::LayerBatch> layer_plan;   // the fused call's hit rows
+    PlanVec<kvm::SeqBatch> key_plan;       // ... and their unpack-order keys
+    PlanVec<kvm::MergeBatch> merge_plan;   // merge, and the fused call's miss rows
     std::string last_error;
 };
 
@@ -194,6 +234,26 @@ void dev_free(kvm_ctx* c, T*& p, size_t count)
     p = nullptr;
 }
 
+// Give up a buffer that launches already enqueued may still read: it stays
+// allocated (and counted) until free_retired.
+template <class T>
+void dev_retire(kvm_ctx* c, T*& p, size_t count)
+{
+    if (!p) return;
+    c->retired.emplace_back(static_cast<void*>(p), count * sizeof(T));
+    p = nullptr;
+}
+
+// Only after a device synchronisation.
+void free_retired(kvm_ctx* c)
+{
+    for (const auto& r : c->retired) {
+        (void)hipFree(r.first);
+        c->device_bytes -= int64_t(r.second);
+    }
+    c->retired.clear();
+}
+
 // Widest move unit (16, 8, 4, 2, 1 bytes) that divides every value OR-ed in.
 int move_unit(uint64_t bits)
 {
@@ -233,15 +293,13 @@ PoolGeom geom_of(const kvm_pool_layout* p)
 }
 
 // The sequences of one call that own at least one tile, with their tile
-// counts, split into launch batches of at most kvm::kRecsPerLaunch.
-struct SeqPlan {
-    std::vector<kvm::SeqBatch> batches;
-    uint64_t align_bits = 0;
-};
-
+// counts, split into launch batches of at most kvm::kRecsPerLaunch (into
+// `batches`, which it clears first); *align_bits ORs their pointers and
+// strides.
 int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs, int32_t n,
-              bool per_layer_tiles, SeqPlan* plan)
+              bool per_layer_tiles, PlanVec<kvm::SeqBatch>& batches, uint64_t* align_bits)
 {
+    batches.clear();
     if (n < 0) return KVM_EINVAL;
     if (n > 0 && !seqs) return KVM_EINVAL;
     if (n > kMaxSeqs) return KVM_ERANGE;
@@ -256,12 +314,8 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
         if (ts < dense) return KVM_EINVAL;
         const int64_t nb = (s.num_tokens + p->block_tokens - 1) / p->block_tokens;
         const int64_t tiles = per_layer_tiles ? nb * num_layers : nb;
-        if (plan->batches.empty() || plan->batches.back().n == kvm::kRecsPerLaunch) {
-            plan->batches.emplace_back();
-            kvm::SeqBatch& nb_ = plan->batches.back();
-            std::memset(&nb_, 0, sizeof(nb_));
-        }
-        kvm::SeqBatch& b = plan->batches.back();
+        if (batches.empty() || batches.back().n == kvm::kRecsPerLaunch) batches.add();
+        kvm::SeqBatch& b = batches.back();
         // unpack launches at most one work item per (tile, side)
         const int64_t items_per_tile = per_layer_tiles ? 1 : p->num_sides;
         if ((b.tile0[b.n] + tiles) * items_per_tile > kMaxTiles) return KVM_ERANGE;
@@ -273,7 +327,7 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
         ++b.n;
         bits |= uint64_t(uintptr_t(s.full)) | uint64_t(ts);
     }
-    plan->align_bits = bits;
+    *align_bits = bits;
     return KVM_OK;
 }
 
@@ -291,32 +345,90 @@ void order_release(kvm_ctx* c)
     c->count_done = nullptr;
 }
 
-std::vector<char> order_key(const kvm::SeqBatch& b, int64_t num_blocks)
+// The key of an unpack order: the pool's block count, then the batch's first
+// tiles and records, byte for byte. A lookup compares a 64-bit hash of it
+// first and the bytes only where the hash matches; the key is never built.
+size_t key_bytes(const kvm::SeqBatch& b)
 {
-    std::vector<char> k(sizeof(int64_t) * (b.n + 2) + sizeof(kvm::SeqRec) * b.n);
-    char* p = k.data();
-    std::memcpy(p, &num_blocks, sizeof(int64_t));
-    std::memcpy(p + sizeof(int64_t), b.tile0, sizeof(int64_t) * (b.n + 1));
-    std::memcpy(p + sizeof(int64_t) * (b.n + 2), b.rec, sizeof(kvm::SeqRec) * b.n);
-    return k;
+    return sizeof(int64_t) * (size_t(b.n) + 2) + sizeof(kvm::SeqRec) * size_t(b.n);
 }
 
-// Before a call on `st` that reads a cached order or the group scratch: the
-// first call on a stream other than the first one waits for the device, since
-// the launches on the first stream recorded no events.
-int enter_stream(kvm_ctx* c, SingleStream* m, hipStream_t st)
+uint64_t mix_words(uint64_t h, const void* p, size_t bytes)  // bytes: a multiple of 8
 {
-    if (m->multi) return KVM_OK;
+    const unsigned char* q = static_cast<const unsigned char*>(p);
+    for (size_t i = 0; i < bytes; i += 8) {
+        uint64_t w;
+        std::memcpy(&w, q + i, 8);
+        h = (h ^ w) * 0x9E3779B97F4A7C15ull;
+        h ^= h >> 29;
+    }
+    return h;
+}
+
+uint64_t order_hash(const kvm::SeqBatch& b, int64_t num_blocks)
+{
+    static_assert(sizeof(kvm::SeqRec) % 8 == 0, "records hash as 64-bit words");
+    uint64_t h = mix_words(0x243F6A8885A308D3ull, &num_blocks, sizeof(int64_t));
+    h = mix_words(h, b.tile0, sizeof(int64_t) * (size_t(b.n) + 1));
+    return mix_words(h, b.rec, sizeof(kvm::SeqRec) * size_t(b.n));
+}
+
+bool key_equals(const std::vector<char>& k, const kvm::SeqBatch& b, int64_t num_blocks)
+{
+    if (k.size() != key_bytes(b)) return false;
+    const char* p = k.data();
+    return std::memcmp(p, &num_blocks, sizeof(int64_t)) == 0 &&
+           std::memcmp(p + sizeof(int64_t), b.tile0, sizeof(int64_t) * (size_t(b.n) + 1)) == 0 &&
+           std::memcmp(p + sizeof(int64_t) * (size_t(b.n) + 2), b.rec,
+                       sizeof(kvm::SeqRec) * size_t(b.n)) == 0;
+}
+
+void key_store(std::vector<char>& k, const kvm::SeqBatch& b, int64_t num_blocks)
+{
+    k.resize(key_bytes(b));  // keeps its capacity
+    char* p = k.data();
+    std::memcpy(p, &num_blocks, sizeof(int64_t));
+    std::memcpy(p + sizeof(int64_t), b.tile0, sizeof(int64_t) * (size_t(b.n) + 1));
+    std::memcpy(p + sizeof(int64_t) * (size_t(b.n) + 2), b.rec, sizeof(kvm::SeqRec) * size_t(b.n));
+}
+
+// Before a call on `st` that reads a cached order or the batched-copy
+// scratch. The launches on the first stream recorded no events, so at the
+// first call on another stream nothing tells when they end. Rather than wait
+// for the device, that call retires every buffer they may still read (the
+// order arrays and the sort's counters, or the copy scratch: freed at the
+// next device synchronisation) and starts on fresh ones, which it allocates;
+// from then on every call records events (see note_reader, kvm_batch_copy).
+void retire_order_scratch(kvm_ctx* c)
+{
+    for (OrderSlot& o : c->orders) {
+        dev_retire(c, o.order, size_t(o.cap));
+        o.cap = 0;
+        o.valid = false;
+    }
+    dev_retire(c, c->d_count, size_t(c->count_cap));
+    c->count_cap = 0;
+    c->count_pending = false;
+}
+
+void retire_copy_scratch(kvm_ctx* c)
+{
+    dev_retire(c, c->d_copy, size_t(c->copy_words));
+    c->copy_words = 0;
+    c->copy_pending = false;
+}
+
+void enter_stream(kvm_ctx* c, SingleStream* m, hipStream_t st, void (*retire)(kvm_ctx*))
+{
+    if (m->multi) return;
     if (!m->seen) {
         m->home = st;
         m->seen = true;
-        return KVM_OK;
+        return;
     }
-    if (st == m->home) return KVM_OK;
-    const hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail_hip(c, e, "hipDeviceSynchronize");
+    if (st == m->home) return;
+    retire(c);
     m->multi = true;
-    return KVM_OK;
 }
 
 // Wait on the host until every launch that read the slot's order has run.
@@ -361,12 +473,11 @@ int note_reader(kvm_ctx* c, OrderSlot* o, hipStream_t st)
 int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStream_t st,
                  OrderSlot** out)
 {
-    const int rc = enter_stream(c, &c->order_streams, st);
-    if (rc != KVM_OK) return rc;
-    std::vector<char> key = order_key(b, num_blocks);
+    enter_stream(c, &c->order_streams, st, retire_order_scratch);
+    const uint64_t hash = order_hash(b, num_blocks);
     ++c->order_tick;
     for (OrderSlot& o : c->orders) {
-        if (o.valid && o.key == key) {
+        if (o.valid && o.hash == hash && key_equals(o.key, b, num_blocks)) {
             if (o.stream != st && o.ready_set) {
                 hipError_t e = hipStreamWaitEvent(st, o.ready, 0);
                 if (e != hipSuccess) return fail_hip(c, e, "hipStreamWaitEvent");
@@ -392,29 +503,28 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
         return fail_hip(c, e, "hipEventCreateWithFlags");
     }
     if (o->cap < ntiles) {
-        // launches on the order's own stream carry no events: let them finish
-        if (o->order && (e = hipDeviceSynchronize()) != hipSuccess)
-            return fail_hip(c, e, "hipDeviceSynchronize");
-        dev_free(c, o->order, size_t(o->cap));
+        // launches on the order's own stream may still read the old array
+        // (they recorded no events): retire it; sizes grow at least 2x
+        const int64_t cap = std::max(ntiles, 2 * o->cap);
+        dev_retire(c, o->order, size_t(o->cap));
         o->cap = 0;
-        if (!dev_alloc(c, &o->order, size_t(ntiles))) {
+        if (!dev_alloc(c, &o->order, size_t(cap))) {
             c->last_error = "hipMalloc: unpack order";
             return KVM_ENOMEM;
         }
-        o->cap = ntiles;
+        o->cap = cap;
     }
     const int64_t words = 2 * (num_blocks + 2);
     if (c->count_cap < words) {
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return fail_hip(c, e, "hipDeviceSynchronize");
-        dev_free(c, c->d_count, size_t(c->count_cap));
+        const int64_t cap = std::max(words, 2 * c->count_cap);
+        dev_retire(c, c->d_count, size_t(c->count_cap));
         c->count_cap = 0;
         c->count_pending = false;
-        if (!dev_alloc(c, &c->d_count, size_t(words))) {
+        if (!dev_alloc(c, &c->d_count, size_t(cap))) {
             c->last_error = "hipMalloc: unpack order scratch";
             return KVM_ENOMEM;
         }
-        c->count_cap = words;
+        c->count_cap = cap;
     }
     if (!c->count_done &&
         (e = hipEventCreateWithFlags(&c->count_done, hipEventDisableTiming)) != hipSuccess) {
@@ -436,7 +546,8 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
         c->count_stream = st;
         c->count_pending = true;
     }
-    o->key = std::move(key);
+    key_store(o->key, b, num_blocks);
+    o->hash = hash;
     o->stream = st;
     o->used = c->order_tick;
     o->valid = true;
@@ -444,14 +555,15 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     return KVM_OK;
 }
 
+// The batched-copy scratch, grown to at least `words` (2x at least): the old
+// buffer is retired, since launches enqueued earlier may still read it.
 int grow_copy(kvm_ctx* c, int64_t words)
 {
     if (words <= c->copy_words) return KVM_OK;
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail_hip(c, e, "hipDeviceSynchronize");
-    if (c->d_copy) dev_free(c, c->d_copy, size_t(c->copy_words));
+    const int64_t cap = std::max<int64_t>({words, 2 * c->copy_words, 8192});
+    dev_retire(c, c->d_copy, size_t(c->copy_words));
     c->copy_words = 0;
-    const int64_t cap = std::max<int64_t>(words, 8192);
+    c->copy_pending = false;
     if (!dev_alloc(c, &c->d_copy, size_t(cap))) {
         c->last_error = "hipMalloc: batched-copy scratch";
         return KVM_ENOMEM;
@@ -602,11 +714,12 @@ int check_copy_list(kvm_ctx* ctx, hipStream_t st, uintptr_t dst_base, uint64_t d
 // merge_layer records split into launch batches, with the widest move unit
 // that divides every pointer and stride seen.
 struct MergePlan {
-    explicit MergePlan(int64_t rb)
+    MergePlan(int64_t rb, PlanVec<kvm::MergeBatch>& store)
         : row_bytes(rb), wide(rb < kMergeShortRow),
           rows_per_tile(int32_t(std::max<int64_t>(1, (wide ? kMergeShortTileBytes : kMergeTileBytes) / rb))),
-          bits(uint64_t(rb))
+          bits(uint64_t(rb)), batches(store)
     {
+        batches.clear();
     }
 
     int add(const void* hit, int64_t hit_stride, int64_t t_hit, const void* miss,
@@ -618,10 +731,7 @@ struct MergePlan {
         const int64_t t_all = t_hit + t_miss;
         if (t_all == 0) return KVM_OK;
         if (!out) return KVM_EINVAL;
-        if (batches.empty() || batches.back().n == kvm::kRecsPerLaunch) {
-            batches.emplace_back();
-            std::memset(&batches.back(), 0, sizeof(kvm::MergeBatch));
-        }
+        if (batches.empty() || batches.back().n == kvm::kRecsPerLaunch) batches.add();
         kvm::MergeBatch& b = batches.back();
         const int64_t tiles = (t_all + rows_per_tile - 1) / rows_per_tile;
         if (b.tile0[b.n] + tiles > kMaxTiles) return KVM_ERANGE;
@@ -654,7 +764,7 @@ struct MergePlan {
     bool wide;
     int32_t rows_per_tile;
     uint64_t bits;
-    std::vector<kvm::MergeBatch> batches;
+    PlanVec<kvm::MergeBatch>& batches;
 };
 
 }  // namespace
@@ -739,6 +849,7 @@ void kvm_destroy(kvm_ctx* ctx)
     if (!ctx) return;
     DeviceGuard guard(ctx->device);
     (void)hipDeviceSynchronize();
+    free_retired(ctx);
     order_release(ctx);
     if (ctx->copy_done) (void)hipEventDestroy(ctx->copy_done);
     if (ctx->d_copy) dev_free(ctx, ctx->d_copy, size_t(ctx->copy_words));
@@ -754,8 +865,16 @@ int kvm_ctx_reserve(kvm_ctx* ctx, int64_t max_seqs, int64_t max_descs)
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
     // group sums and bases, and the records of one piece per object (objects
-    // of up to 128 KiB)
-    return grow_copy(ctx, kvm::copy_group_words(max_descs) + 3 * std::min(max_descs, kMaxPieces));
+    // of up to 128 KiB); a set-up call, so it may wait for the device and
+    // free what move calls retired
+    const int64_t words = kvm::copy_group_words(max_descs) + 3 * std::min(max_descs, kMaxPieces);
+    if (words <= ctx->copy_words && ctx->retired.empty()) return KVM_OK;
+    const hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail_hip(ctx, e, "hipDeviceSynchronize");
+    free_retired(ctx);
+    const int rc = grow_copy(ctx, words);
+    free_retired(ctx);  // the scratch it replaced: the device is idle
+    return rc;
 }
 
 int kvm_ctx_reserve_unpack(kvm_ctx* ctx, int64_t max_tiles, int64_t max_pool_blocks)
@@ -766,6 +885,7 @@ int kvm_ctx_reserve_unpack(kvm_ctx* ctx, int64_t max_tiles, int64_t max_pool_blo
     if (!guard.ok()) return KVM_EHIP;
     hipError_t e = hipDeviceSynchronize();  // no order or count array may be in use
     if (e != hipSuccess) return fail_hip(ctx, e, "hipDeviceSynchronize");
+    free_retired(ctx);
     for (OrderSlot& o : ctx->orders) {
         if (!o.ready && (e = hipEventCreateWithFlags(&o.ready, hipEventDisableTiming)) != hipSuccess) {
             o.ready = nullptr;
@@ -831,6 +951,7 @@ int kvm_take_device_errors(kvm_ctx* ctx, int64_t* count)
     if (!guard.ok()) return KVM_EHIP;
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail_hip(ctx, e, "hipDeviceSynchronize");
+    free_retired(ctx);
     unsigned long long v = 0;
     e = hipMemcpy(&v, ctx->d_err, sizeof(v), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return fail_hip(ctx, e, "hipMemcpy (error counter)");
@@ -848,12 +969,13 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
     int rc = check_layout(layout, num_layers);
     if (rc != KVM_OK) return rc;
     if (!pack && (layer < 0 || layer >= num_layers)) return KVM_ERANGE;
-    SeqPlan plan;
-    rc = plan_seqs(layout, num_layers, seqs, n, pack, &plan);
+    PlanVec<kvm::SeqBatch>& batches = ctx->seq_plan;
+    uint64_t align_bits = 0;
+    rc = plan_seqs(layout, num_layers, seqs, n, pack, batches, &align_bits);
     if (rc != KVM_OK) return rc;
-    if (plan.batches.empty()) return KVM_OK;
+    if (batches.empty()) return KVM_OK;
     if (!pool) return KVM_EINVAL;
-    const uint64_t bits = plan.align_bits | uint64_t(uintptr_t(pool)) | uint64_t(layout->row_bytes) |
+    const uint64_t bits = align_bits | uint64_t(uintptr_t(pool)) | uint64_t(layout->row_bytes) |
                           uint64_t(layout->block_stride) | uint64_t(layout->side_stride) |
                           uint64_t(layout->layer_stride);
     const int unit = move_unit(bits);
@@ -863,14 +985,14 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (ctx->checks && !pack) {
         std::vector<std::pair<const int32_t*, int64_t>> tables;
-        for (const kvm::SeqBatch& b : plan.batches)
+        for (const kvm::SeqBatch& b : batches)
             for (int32_t i = 0; i < b.n; ++i)
                 tables.emplace_back(b.rec[i].block_table, b.tile0[i + 1] - b.tile0[i]);
         rc = check_unique_blocks(ctx, st, tables, layout->num_blocks);
         if (rc != KVM_OK) return rc;
     }
     const PoolGeom g = geom_of(layout);
-    std::vector<OrderSlot*> orders(plan.batches.size(), nullptr);
+    OrderSlot* orders[kOrderSlots] = {};
     if (!pack) {
         // Each batch holds its own cache slot for the whole call, so a call may
         // have at most kOrderSlots batches. Sorting runs first, so that a
@@ -878,16 +1000,16 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
         // only the context's own scratch). The counting sort costs O(blocks);
         // for a pool much larger than the call's tiles the tiles keep their
         // own order instead.
-        if (plan.batches.size() > size_t(kOrderSlots)) return KVM_ERANGE;
-        for (size_t i = 0; i < plan.batches.size(); ++i) {
-            const int64_t ntiles = plan.batches[i].tile0[plan.batches[i].n];
+        if (batches.size() > size_t(kOrderSlots)) return KVM_ERANGE;
+        for (size_t i = 0; i < batches.size(); ++i) {
+            const int64_t ntiles = batches[i].tile0[batches[i].n];
             if (layout->num_blocks > 16 * ntiles + 65536) continue;
-            rc = unpack_order(ctx, plan.batches[i], layout->num_blocks, st, &orders[i]);
+            rc = unpack_order(ctx, batches[i], layout->num_blocks, st, &orders[i]);
             if (rc != KVM_OK) return rc;
         }
     }
-    for (size_t i = 0; i < plan.batches.size(); ++i) {
-        const kvm::SeqBatch& b = plan.batches[i];
+    for (size_t i = 0; i < batches.size(); ++i) {
+        const kvm::SeqBatch& b = batches[i];
         hipError_t e;
         if (pack) {
             e = kvm::launch_pack(unit, g, static_cast<const char*>(pool), num_layers, b, ctx->d_err,
@@ -924,7 +1046,7 @@ int kvm_merge_layer(kvm_ctx* ctx, int64_t row_bytes, const kvm_merge_seq* seqs, 
     if (!ctx || row_bytes < 1 || n < 0) return KVM_EINVAL;
     if (n > 0 && !seqs) return KVM_EINVAL;
     if (n > kMaxSeqs || row_bytes > INT32_MAX) return KVM_ERANGE;
-    MergePlan plan(row_bytes);
+    MergePlan plan(row_bytes, ctx->merge_plan);
     for (int32_t i = 0; i < n; ++i) {
         const kvm_merge_seq& m = seqs[i];
         const int rc = plan.add(m.hit, m.hit_stride, m.t_hit, m.miss, m.miss_stride, m.t_miss,
@@ -951,9 +1073,11 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
     if (c_kv > INT32_MAX) return KVM_ERANGE;
     const int64_t dense = int64_t(num_layers) * c_kv;
     // hit rows: tiles of the fused kernel; miss rows: a merge with no hit part
-    std::vector<kvm::LayerBatch> hit;
-    std::vector<kvm::SeqBatch> keys;   // the same records as an unpack call, for the tile order
-    MergePlan miss(c_kv);
+    PlanVec<kvm::LayerBatch>& hit = ctx->layer_plan;
+    PlanVec<kvm::SeqBatch>& keys = ctx->key_plan;  // the same records as an unpack call, for the tile order
+    hit.clear();
+    keys.clear();
+    MergePlan miss(c_kv, ctx->merge_plan);
     uint64_t bits = uint64_t(uintptr_t(pool)) | uint64_t(layout->row_bytes) |
                     uint64_t(layout->block_stride) | uint64_t(layout->side_stride) |
                     uint64_t(layout->layer_stride);
@@ -974,10 +1098,8 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
         }
         if (s.t_hit == 0) continue;
         if (hit.empty() || hit.back().n == kvm::kRecsPerLaunch) {
-            hit.emplace_back();
-            keys.emplace_back();
-            std::memset(&hit.back(), 0, sizeof(kvm::LayerBatch));
-            std::memset(&keys.back(), 0, sizeof(kvm::SeqBatch));
+            hit.add();
+            keys.add();
         }
         kvm::LayerBatch& b = hit.back();
         kvm::SeqBatch& k = keys.back();
@@ -1008,7 +1130,7 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
         rc = check_unique_blocks(ctx, st, tables, layout->num_blocks);
         if (rc != KVM_OK) return rc;
     }
-    std::vector<OrderSlot*> orders(hit.size(), nullptr);
+    OrderSlot* orders[kOrderSlots] = {};
     for (size_t i = 0; i < hit.size(); ++i) {
         if (layout->num_blocks > 16 * hit[i].tile0[hit[i].n] + 65536) continue;
         rc = unpack_order(ctx, keys[i], layout->num_blocks, st, &orders[i]);
@@ -1063,8 +1185,8 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     // one group or one workgroup per object: no scratch
     const bool scratch = !one_group && !a.each;
     if (scratch) {
-        int rc = enter_stream(ctx, &ctx->copy_streams, st);
-        if (rc == KVM_OK) rc = grow_copy(ctx, kvm::copy_group_words(n_descs) + 3 * piece_cap);
+        enter_stream(ctx, &ctx->copy_streams, st, retire_copy_scratch);
+        const int rc = grow_copy(ctx, kvm::copy_group_words(n_descs) + 3 * piece_cap);
         if (rc != KVM_OK) return rc;
     }
     a.dst = static_cast<char*>(dst_base);

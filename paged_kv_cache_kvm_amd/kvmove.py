@@ -3,7 +3,10 @@
 Argument marshalling only: every move runs in the library's HIP kernels. Device
 buffers are passed as integer device addresses or as torch tensors (their
 data_ptr); streams as a torch stream, an integer hipStream_t, or None for the
-current torch stream. Each call raises KvmError on a non-zero status.
+current torch stream. Record lists (kvm_seq, kvm_merge_seq, kvm_layer_seq) are
+passed as a list, or as a ctypes array built once with records() and reused
+by later calls (a per-layer loop), which saves building it on every call. Each
+call raises KvmError on a non-zero status.
 
 The library must be built (paged_kv_cache_kvm_amd/build.py): the first call
 into it raises if libkvmove.so is missing, and there is no fallback path.
@@ -119,10 +122,21 @@ def _addr(x) -> int | None:
     raise TypeError(f"expected a device address or tensor, got {type(x).__name__}")
 
 
+_current_raw_stream = None
+
+
 def _stream(s) -> int | None:
+    global _current_raw_stream
     if s is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _current_raw_stream is None:
+            import torch
+            raw, dev = (getattr(torch._C, "_cuda_getCurrentRawStream", None),
+                        getattr(torch._C, "_cuda_getDevice", None))
+            if raw is not None and dev is not None:
+                _current_raw_stream = lambda: raw(dev())
+            else:
+                _current_raw_stream = lambda: torch.cuda.current_stream().cuda_stream
+        return _current_raw_stream()
     if isinstance(s, int):
         return s
     return s.cuda_stream
@@ -212,7 +226,22 @@ def layer_seq(block_table, full, t_hit: int, miss, miss_stride: int, t_miss: int
                          miss_stride, t_miss, _addr(out), out_stride)
 
 
-def _array(cls, items: Sequence):
+def records(items: Sequence):
+    """A ctypes array of the given records (all of one type: kvm_seq,
+    kvm_merge_seq or kvm_layer_seq), for calls that pass the same records
+    again and again."""
+    items = list(items)
+    if not items:
+        raise ValueError("records() needs at least one record; pass [] to a call instead")
+    return (type(items[0]) * len(items))(*items)
+
+
+def _array(cls, items):
+    if isinstance(items, ctypes.Array):
+        if items._type_ is not cls:
+            raise TypeError(f"expected an array of {cls.__name__}, got one of "
+                            f"{items._type_.__name__}")
+        return items, len(items)
     items = list(items)
     arr = (cls * max(1, len(items)))(*items)
     return arr, len(items)

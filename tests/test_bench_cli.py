@@ -32,20 +32,43 @@ def test_quantile_interpolates():
     assert abs(b.quantile(xs, 0.5) - 2.5) < 1e-12
 
 
-def test_traffic_only_for_matching_kernel_sources():
-    """The committed traffic summary is used only while the kernel sources hash
-    to the hash it records; a summary of other sources reports nothing."""
+def test_traffic_only_for_matching_kernel_sources(tmp_path, monkeypatch):
+    """A traffic summary under profiles/ is used only while the kernel sources
+    hash to the hash it records; a summary of other sources reports nothing,
+    and an op no current summary has reports nothing."""
+    import json
     b = _bench()
-    got = b.measured_traffic("unpack_layer")
-    text = open(b.PROFILE).read()
-    import hashlib
-    h = hashlib.sha256()
-    for f in b.KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if h.hexdigest() in text:
-        assert isinstance(got, int) and got > 0
-    else:
-        assert got is None
+    h = b.kernel_source_sha256()
+    (tmp_path / "current.md").write_text(
+        "text\ntraffic-json: " + json.dumps({"kernel_source_sha256": h,
+                                            "bytes_per_launch": {"merge_layer": 123}}) + "\n")
+    (tmp_path / "stale.md").write_text(
+        "traffic-json: " + json.dumps({"kernel_source_sha256": "0" * 64,
+                                       "bytes_per_launch": {"unpack_layer": 456}}) + "\n")
+    monkeypatch.setattr(b, "PROFILES", str(tmp_path))
+    assert b.measured_traffic("merge_layer") == 123
+    assert b.measured_traffic("unpack_layer") is None
+    assert b.measured_traffic("pack_full") is None
+    monkeypatch.setattr(b, "PROFILES", str(tmp_path / "missing"))
+    assert b.measured_traffic("merge_layer") is None
+
+
+def test_committed_traffic_matches_its_sources():
+    """Each committed traffic line either matches the sources built now (and
+    then gives positive byte counts) or is ignored."""
+    import glob
+    import json
+    b = _bench()
+    h = b.kernel_source_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic-json: "):
+                continue
+            rec = json.loads(line[len("traffic-json: "):])
+            for op, v in rec["bytes_per_launch"].items():
+                got = b.measured_traffic(op)
+                if rec["kernel_source_sha256"] == h:
+                    assert isinstance(got, int) and got > 0, (path, op)
 
 
 def test_profile_commands_run_committed_files_with_known_flags():

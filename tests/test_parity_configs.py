@@ -120,7 +120,21 @@ def test_llama8b_layer_loop(ctx, gpu, fused):
         cm = complete[r * L * t_all * C:(r + 1) * L * t_all * C].view(L, t_all, C)
         for l in range(L):
             assert torch.equal(pk[:t_hit, l], cm[l, :t_hit]), f"layer {l} request {r}"
-    del pool, fbs, misses, complete, packed
+    # Every layer, side and request, every token (the miss tokens t >= T_hit too),
+    # by pack's definition on the final pool: packed[r][t][l][s] is the slot row
+    # pool[l][s][bt[t / B]][t % B], gathered with torch from the block table.
+    say("  checking pack_full == pool[l][s][bt[t/B]][t%B] for every token, layer and side")
+    pv = pool.view(L, S, N, B, rb)
+    for r in range(R):
+        pk = packed[r].view(t_all, L, S, rb)
+        bt_l = bts[r].long()
+        for t0 in range(0, t_all, 4096):
+            t = torch.arange(t0, min(t_all, t0 + 4096), device=gpu)
+            rows = pv[:, :, bt_l[t // B], t % B]            # [L][S][tokens][rb]
+            assert torch.equal(pk[t0:t0 + len(t)], rows.permute(2, 0, 1, 3)), \
+                f"pack_full request {r} tokens [{t0}, {t0 + len(t)})"
+            del rows
+    del pool, pv, fbs, misses, complete, packed
     torch.cuda.empty_cache()
 
 
@@ -238,7 +252,7 @@ def test_mla_agentic_layer_loop(ctx, gpu, fused):
     roff = np.concatenate([[0], np.cumsum([t * C for t in w.t_all])])
     layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, 0, N)
     seqs = [kv.seq(bts[r], fbs[r], w.t_hit[r]) for r in range(R)]
-    sample_layers = (0, L - 1)
+    sample_layers = (0, L // 2, L - 1)
     ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, 0, N)
     for l in range(L):
         pre = host(slot) if l in sample_layers else None

@@ -471,6 +471,74 @@ def test_copy_scratch_second_stream_waits(gpu):
         c.close()
 
 
+def test_move_calls_do_not_wait_for_the_device(gpu):
+    """No move call waits for the whole device. While a slow batched copy
+    (one workgroup, 1 GiB) runs on stream a, calls on stream b grow the unpack
+    order (a bigger record set), grow the batched-copy scratch as the first
+    copy on a second stream, and an unpack on a takes the order cache's second
+    stream: all of them return while a's copy is still running (its event is
+    not complete). Every result is then compared with the oracle."""
+    say("  move calls beside a slow copy on another stream")
+    c = kv.Context(0)
+    try:
+        L, S, N, B, rb = 2, 2, 2000, 16, 256
+        layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+        ref = oracle.pool_struct(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
+        rng = np.random.default_rng(83)
+        Ts = [1000, 20000]
+        tables = wl.block_tables(83, 1, N, [wl.blocks_needed(t, B) for t in Ts])
+        fb_np = [rng.integers(0, 256, t * L * S * rb, dtype=np.uint8) for t in Ts]
+        want_pool = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
+        bts, fbs = [up(t, gpu) for t in tables], [up(f, gpu) for f in fb_np]
+        pool = up(want_pool, gpu)
+
+        big = 1 << 30                               # the slow copy: 16,384 objects of 64 KiB
+        slow_lens = np.full(big >> 16, 1 << 16, np.int64)
+        slow_d = np.stack([np.arange(len(slow_lens)) << 16,
+                           np.arange(len(slow_lens))[::-1].copy() << 16, slow_lens],
+                          axis=1).astype(np.uint64)
+        slow_src = torch.randint(0, 256, (big,), dtype=torch.uint8, device=gpu)
+        slow_dst = torch.empty(big, dtype=torch.uint8, device=gpu)
+        arena = 1 << 26                             # a list that outgrows the scratch
+        lens = 256 * rng.integers(1, 4, size=40_000)
+        fast_d = np.stack([wl.placements(84, 1, lens, arena), wl.placements(84, 2, lens, arena),
+                           lens], axis=1).astype(np.uint64)
+        src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+        src, dst = up(src_np, gpu), up(np.full(arena, SENTINEL, np.uint8), gpu)
+        dd_slow, dd_fast = up(slow_d.view(np.uint8), gpu), up(fast_d.view(np.uint8), gpu)
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        done_a = torch.cuda.Event()
+        torch.cuda.synchronize()
+
+        kv.kvm_unpack_layer(c.handle, layout, pool, L, 0, [kv.seq(bts[0], fbs[0], Ts[0])], stream=b)
+        oracle.unpack_layer(want_pool, ref, L, 0, tables[0], Ts[0], fb_np[0])
+        torch.cuda.synchronize()
+        c.set_max_workgroups(1)
+        kv.kvm_batch_copy(c.handle, slow_dst, big, slow_src, big, dd_slow, len(slow_d), stream=a)
+        c.set_max_workgroups(0)
+        done_a.record(a)
+        before = c.device_bytes()
+        kv.kvm_unpack_layer(c.handle, layout, pool, L, 1, [kv.seq(bts[1], fbs[1], Ts[1])], stream=b)
+        kv.kvm_batch_copy(c.handle, dst, arena, src, arena, dd_fast, len(fast_d), stream=b)
+        kv.kvm_unpack_layer(c.handle, layout, pool, L, 0, [kv.seq(bts[1], fbs[1], Ts[1])], stream=a)
+        still_running = not done_a.query()
+        grown = c.device_bytes() > before
+        torch.cuda.synchronize()
+        assert still_running, "a move call on stream b waited for stream a's copy"
+        assert grown, "the calls were meant to grow the scratch"
+        oracle.unpack_layer(want_pool, ref, L, 1, tables[1], Ts[1], fb_np[1])
+        oracle.unpack_layer(want_pool, ref, L, 0, tables[1], Ts[1], fb_np[1])
+        assert np.array_equal(down(pool), want_pool)
+        want_dst = np.full(arena, SENTINEL, np.uint8)
+        oracle.batch_copy(want_dst, src_np, fast_d)
+        assert np.array_equal(down(dst), want_dst)
+        assert torch.equal(slow_dst.view(-1, 1 << 16).flip(0).reshape(-1), slow_src)
+        assert c.take_device_errors() == 0
+        assert c.device_bytes() <= before + (64 << 20)   # set-aside scratch freed again
+    finally:
+        c.close()
+
+
 def test_more_items_than_one_dispatch_holds(ctx, gpu):
     """4.3 M one-token blocks of 16 bytes: pack, unpack and fused items beyond
     the 4,194,303 workgroups of 1024 threads a dispatch can count, so the
