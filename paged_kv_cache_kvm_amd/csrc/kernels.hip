@@ -952,13 +952,35 @@ __device__ __forceinline__ void wave_copy(const char* __restrict__ s, char* __re
 }
 
 // One piece by one 1024-thread workgroup: wavefront w moves bytes
-// [w*8 KiB, (w+1)*8 KiB) of the piece, each lane 8 vectors 1 KiB apart.
+// [w*8 KiB, (w+1)*8 KiB) of the piece, each lane 8 vectors 1 KiB apart
+// (pieces of at most 64 KiB: [w*4 KiB, (w+1)*4 KiB), 4 vectors per lane).
 __device__ __forceinline__ void copy_piece(uint64_t src, uint64_t dst, uint64_t nbytes)
 {
     constexpr int kUnr = int(kPieceBytes / (16 * 1024));
     const V16* s = reinterpret_cast<const V16*>(src);
     V16* d = reinterpret_cast<V16*>(dst);
     const uint32_t nv = uint32_t(nbytes >> 4);
+    // A piece of at most 64 KiB (an object of 16-64 KiB): every wavefront
+    // moves 4 vectors per lane instead of half of them moving 8 (+0.9 % on
+    // objects of 4-128 KiB, the same elsewhere, measured on MI355X).
+    if (nv <= 1024 * 4) {
+        constexpr int kU4 = 4;
+        const uint32_t first4 = (threadIdx.x >> 6) * (64 * kU4) + (threadIdx.x & 63);
+        for (uint32_t base = first4; base < nv + 1024 * kU4; base += 1024 * kU4) {
+            V16 v[kU4];
+#pragma unroll
+            for (int k = 0; k < kU4; ++k) {
+                const uint32_t j = base + k * 64;
+                if (j < nv) v[k] = ld(s + j);
+            }
+#pragma unroll
+            for (int k = 0; k < kU4; ++k) {
+                const uint32_t j = base + k * 64;
+                if (j < nv) st(d + j, v[k]);
+            }
+        }
+        return;
+    }
     const uint32_t first = (threadIdx.x >> 6) * (64 * kUnr) + (threadIdx.x & 63);
     // One pass over the piece (it is at most 1024 * kUnr vectors), written as
     // a loop whose bound the compiler cannot reduce to one trip: every
@@ -1035,9 +1057,11 @@ __global__ __launch_bounds__(1024, 8) void k_bc_copy(const CopyDesc* __restrict_
                 if (s_incl[mid] > b) hi = mid;
                 else lo = mid + 1;
             }
-            const unsigned long long j = b - (lo ? s_incl[lo - 1] : 0);
-            copy_piece(s_src[lo] + j * kPieceBytes, s_dst[lo] + j * kPieceBytes,
-                       min(uint64_t(kPieceBytes), s_len[lo] - j * kPieceBytes));
+            // the same in every lane: keep them in scalar registers
+            const unsigned long long j = uniform64(b - (lo ? s_incl[lo - 1] : 0));
+            const uint64_t len = uniform64(s_len[lo]);
+            copy_piece(uniform64(s_src[lo]) + j * kPieceBytes, uniform64(s_dst[lo]) + j * kPieceBytes,
+                       min(uint64_t(kPieceBytes), len - j * kPieceBytes));
         }
         const CopyDesc x = lane < n ? descs[lane] : CopyDesc{0, 0, 0};
         small_len = split_object(x, src, src_bytes, dst, dst_bytes, use_pieces).small;

@@ -132,6 +132,31 @@ def test_batch_copy_random(ctx, gpu):
                    np.full(arena, SENTINEL, np.uint8), d, label="4K-128K objects")
 
 
+@pytest.mark.parametrize("n", [5, 300, 70_000], ids=["one-group", "meta", "three-pass"])
+def test_batch_copy_huge_objects(ctx, gpu, n):
+    """Objects of many pieces (up to 3 MiB, with ragged last pieces) mixed with
+    one-piece, short and unaligned ones: one group, the one-workgroup metadata
+    pass, and the three-launch metadata pass. Sizes straddle the 16 KiB,
+    64 KiB (piece layout) and 128 KiB (piece) boundaries."""
+    rng = np.random.default_rng(90 + n)
+    edge = [1 << 20, (1 << 20) - 16, (1 << 20) + 16, (3 << 20) + 4080, (64 << 10) * 17,
+            (128 << 10) + 16, 16 << 10, 5000]
+    lens = np.array([edge[i % len(edge)] for i in range(min(n, 40))], np.int64)
+    if n > 40:
+        rest = 256 * rng.integers(1, 64, size=n - 40)             # short objects, 256 B - 16 KiB
+        lens = np.concatenate([lens, rest])
+        rng.shuffle(lens)
+    slots = -(-lens // 256) * 256
+    arena = int(slots.sum()) + (8 << 20)
+    d = _descs(wl.placements(91, 1, slots, arena), wl.placements(91, 2, slots, arena), lens)
+    shift = np.zeros(len(lens), bool)
+    shift[3::7] = True
+    shift &= (slots - lens) >= 8                                   # room in the source slot
+    d[shift, 0] += 8                                               # some sources unaligned
+    run_batch_copy(ctx, gpu, rng.integers(0, 256, arena, dtype=np.uint8),
+                   np.full(arena, SENTINEL, np.uint8), d, label=f"huge objects n={n}")
+
+
 def test_batch_copy_alignment_matrix(ctx, gpu):
     """Every (src % 16, dst % 16) pair, with lengths 0..300 and one 1 MiB object."""
     rng = np.random.default_rng(22)
