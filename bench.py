@@ -24,8 +24,12 @@ Inputs are seeded: --seed S (default 1002) draws the layer loop from S, the
 restore list from S+1, the MLA loop from S+2 and the small-object list from
 S+3 (the defaults are the workloads' own seeds).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S] [--no-cpu] [--no-batch-copy]
-                      [--no-host] [--no-pipeline] [--no-mla]
+--verify checks, after each timed section and outside its timing, every
+output of the layer loop, the MLA loop and the two copy lists on the device
+against the operations' definitions (no oracle: plain torch indexing).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S] [--verify] [--no-cpu]
+                      [--no-batch-copy] [--no-host] [--no-pipeline] [--no-mla]
                       [--no-restore] [--no-small]
 """
 from __future__ import annotations
@@ -65,6 +69,9 @@ def parse():
     ap.add_argument("--no-small", action="store_true", help="skip the small-call section")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the layerwise overlap section (workgroup-bounded moves)")
+    ap.add_argument("--verify", action="store_true",
+                    help="after each timed section, check its outputs on the device against the "
+                         "operations' defining properties (untimed; exits 1 on a mismatch)")
     return ap.parse_args()
 
 
@@ -97,6 +104,63 @@ def quantile(xs, q):
     lo = int(pos)
     hi = min(lo + 1, len(xs) - 1)
     return xs[lo] + (xs[hi] - xs[lo]) * (pos - lo)
+
+
+class VerifyError(RuntimeError):
+    pass
+
+
+def expect(ok, what):
+    if not bool(ok):
+        raise VerifyError(what)
+
+
+def verify_layer_loop(torch, s):
+    """The layer loop's outputs on the device, by the operations' definitions:
+    complete_layer[r][l] is the hit slice of layer l then its miss rows; the
+    slot row of every hit token t holds full[r][t][l]; and packed[r][t][l][s]
+    is the pool row pool[l][s][bt[t / B]][t % B] for every token (pack after the
+    loop)."""
+    bts, fbs, misses, complete, packed = s["keep"]
+    sh = s["w"].shape
+    L, S, B, rb, N, C = sh.layers, sh.sides, sh.block_tokens, sh.row_bytes, s["w"].pool_blocks, s["C"]
+    th, tm = s["w"].t_hit[0], s["w"].t_miss[0]
+    ta = th + tm
+    pv = s["pool"].view(L, S, N, B, rb)
+    for r in range(len(fbs)):
+        fb, ms = fbs[r].view(th, L, C), misses[r].view(tm, L, C)
+        cm = complete[r * L * ta * C:(r + 1) * L * ta * C].view(L, ta, C)
+        for l in range(L):
+            expect(torch.equal(cm[l, :th], fb[:, l]), f"complete_layer hit rows, request {r} layer {l}")
+            expect(torch.equal(cm[l, th:], ms[:, l]), f"complete_layer miss rows, request {r} layer {l}")
+        pk, bt = packed[r].view(ta, L, S, rb), bts[r].long()
+        for t0 in range(0, ta, 4096):
+            t = torch.arange(t0, min(ta, t0 + 4096), device=pv.device)
+            rows = pv[:, :, bt[t // B], t % B].permute(2, 0, 1, 3)      # [tokens][L][S][rb]
+            expect(torch.equal(pk[t0:t0 + len(t)], rows), f"pack_full request {r} tokens from {t0}")
+            h = int((t < th).sum().item())
+            if h:
+                expect(torch.equal(rows[:h], fbs[r].view(th, L, S, rb)[t0:t0 + h]),
+                       f"unpack_layer slot rows, request {r} tokens from {t0}")
+            del rows
+
+
+def verify_copies(torch, src, dst, descs_np, granule=256, batch=4096):
+    """Every object of a copy list: dst[dst_off, +n) == src[src_off, +n), on the
+    device. Offsets are multiples of `granule`, so each length is compared
+    through strided windows of the two buffers."""
+    import numpy as np
+    d = torch.from_numpy(descs_np.astype(np.int64)).to(src.device)
+    expect(bool(((d[:, 0] % granule) == 0).all()) and bool(((d[:, 1] % granule) == 0).all()),
+           "offsets are whole granules")
+    for n in np.unique(descs_np[:, 2]):
+        n = int(n)
+        sel = d[d[:, 2] == n]
+        ws, wd = src.unfold(0, n, granule), dst.unfold(0, n, granule)
+        for a in range(0, len(sel), batch):
+            part = sel[a:a + batch]
+            expect(torch.equal(wd[part[:, 1] // granule], ws[part[:, 0] // granule]),
+                   f"an object of {n} bytes differs")
 
 
 def llama_setup(torch, kv, wl, dev, seed):
@@ -412,7 +476,7 @@ def plain_copies(torch, kv, ctx, dev, nbytes=2 << 30, reps=10):
     return torch_copy, stream_copy
 
 
-def batch_copy_section(torch, kv, wl, ctx, dev, seed, reps=10):
+def batch_copy_section(torch, kv, wl, ctx, dev, seed, reps=10, verify=False):
     import dataclasses
     w = dataclasses.replace(wl.SMALL_OBJS, seed=seed)
     descs_np = wl.small_object_descs(w)
@@ -435,6 +499,8 @@ def batch_copy_section(torch, kv, wl, ctx, dev, seed, reps=10):
     ms = ev.mean_ms("batch_copy")
     spread = [round(quantile(ev.all_ms("batch_copy"), q), 4) for q in (0.1, 0.5, 0.9)]
     gbs = 2 * total / (ms * 1e6)
+    if verify:
+        verify_copies(torch, src, dst, descs_np)
     del src, dst, descs
     torch.cuda.empty_cache()
     return {"workload": w.name, "objects": len(descs_np), "bytes_rw": 2 * total,
@@ -447,7 +513,7 @@ def batch_copy_section(torch, kv, wl, ctx, dev, seed, reps=10):
                                  "k_bc_scan2, k_bc_map) and its k_bc_copy launch")}
 
 
-def mla_section(torch, kv, wl, ctx, dev, seed, reps=5):
+def mla_section(torch, kv, wl, ctx, dev, seed, reps=5, verify=False):
     """The MLA agentic layer loop (64 requests, T_hit ~ U{16384..65536},
     T_miss ~ U{128..1024}, 61 layers of one 576-element bf16 latent, B=64, a
     one-layer slot pool): per layer unpack + merge into a 2-deep complete_layer
@@ -546,6 +612,24 @@ def mla_section(torch, kv, wl, ctx, dev, seed, reps=5):
                                f"one launch: HIP events around the op's {L} launches back to "
                                f"back, divided by {L}")
     assert ctx.take_device_errors() == 0
+    if verify:
+        # every layer of one more separate loop, each checked right after its moves
+        slots = slot.view(N, B, C)
+        for l in range(L):
+            kv.kvm_unpack_layer(ctx.handle, layout, slot, L, l, seqs)
+            kv.kvm_merge_layer(ctx.handle, C, merge_l[l])
+            ring = rings[l % 2]
+            mbase = l * miss_all
+            for r in range(R):
+                th = w.t_hit[r]
+                fbl = fbs[r].view(th, L, C)[:, l]
+                o = ring[roff[r]:roff[r + 1]].view(-1, C)
+                expect(torch.equal(o[:th], fbl), f"mla complete_layer hit rows, layer {l} request {r}")
+                expect(torch.equal(o[th:], misses[mbase + moff[r]:mbase + moff[r + 1]].view(-1, C)),
+                       f"mla complete_layer miss rows, layer {l} request {r}")
+                t = torch.arange(th, device=slot.device)
+                expect(torch.equal(slots[bts[r].long()[t // B], t % B], fbl),
+                       f"mla slot rows, layer {l} request {r}")
     del fbs, misses, slot, rings, bts
     torch.cuda.empty_cache()
     return out
@@ -614,7 +698,7 @@ def small_call_section(torch, kv, wl, ctx, dev, calls=2000):
                     "call of kvm_version)"}
 
 
-def restore_section(torch, kv, wl, ctx, dev, seed, reps=10):
+def restore_section(torch, kv, wl, ctx, dev, seed, reps=10, verify=False):
     """The long-sequence restore list (one 128,000-token sequence of a
     Qwen3-32B-like model, L=64, B=64: 256,000 K/V objects of 128 KiB from
     random staging offsets into their paged slots), as one batched copy and as
@@ -663,6 +747,12 @@ def restore_section(torch, kv, wl, ctx, dev, seed, reps=10):
                                out["one_call"]["ms"],
                                "one call: HIP events around its single k_bc_each launch")
     assert ctx.take_device_errors() == 0
+    if verify:
+        for fn in (one_call, per_layer):
+            pool.fill_(0xA5)
+            fn()
+            torch.cuda.synchronize()
+            verify_copies(torch, staging, pool, descs_np)
     del staging, pool, descs
     torch.cuda.empty_cache()
     return out
@@ -824,6 +914,16 @@ def roofline(kernel, op, bytes_per_launch, ms_per_launch, timed):
             "ms_per_launch": round(ms_per_launch, 4), "timed": timed}
 
 
+def run_verify(fn):
+    """Run fn; a VerifyError (an output that breaks its definition) ends the
+    run with status 1 and the failing check on stderr."""
+    try:
+        return fn()
+    except VerifyError as e:
+        log(f"[bench] verify FAILED: {e}")
+        sys.exit(1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -853,6 +953,10 @@ def main():
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / args.steps
     value = step_bytes * args.steps / dt / 1e9
+    verified = {}
+    if args.verify:
+        run_verify(lambda: verify_layer_loop(torch, s))
+        verified["layer_loop"] = "pass"
 
     # per-launch durations: HIP events on the launch stream around a loop of
     # each op alone (its launches back to back), divided by the launch count
@@ -898,9 +1002,17 @@ def main():
     # Plain copies, for reference only: pack and the fused kernel move more than
     # either, so neither bounds the ops and no op is reported as a share of them.
     torch_copy, stream_copy = plain_copies(torch, kv, ctx, dev)
-    mla = None if args.no_mla else mla_section(torch, kv, wl, ctx, dev, args.seed + 2)
-    bc = None if args.no_batch_copy else batch_copy_section(torch, kv, wl, ctx, dev, args.seed + 3)
-    restore = None if args.no_restore else restore_section(torch, kv, wl, ctx, dev, args.seed + 1)
+    mla = None if args.no_mla else run_verify(
+        lambda: mla_section(torch, kv, wl, ctx, dev, args.seed + 2, verify=args.verify))
+    bc = None if args.no_batch_copy else run_verify(
+        lambda: batch_copy_section(torch, kv, wl, ctx, dev, args.seed + 3, verify=args.verify))
+    restore = None if args.no_restore else run_verify(
+        lambda: restore_section(torch, kv, wl, ctx, dev, args.seed + 1, verify=args.verify))
+    if args.verify:
+        for name, sec in (("mla_layer_loop", mla), ("batch_copy", bc),
+                          ("batch_copy_restore", restore)):
+            if sec is not None and "skipped" not in sec:
+                verified[name] = "pass"
     small = None if args.no_small else small_call_section(torch, kv, wl, ctx, dev)
     ctx.close()
     cpu = None if args.no_cpu else cpu_baseline(wl)
@@ -933,6 +1045,7 @@ def main():
         "batch_copy_restore": restore,
         "small_calls": small,
         "cpu_baseline": cpu,
+        "verify": verified if args.verify else None,
         "device": device_info(torch),
     }
     print(json.dumps(out), flush=True)
