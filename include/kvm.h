@@ -207,10 +207,7 @@ void kvm_destroy(kvm_ctx* ctx);
  * + 1) grows the scratch itself, to at least twice its size, without
  * waiting: the old buffer stays allocated until the next device
  * synchronisation below. This call synchronises the device when it resizes
- * the scratch or has such buffers to free, and frees them. The destination
- * order of a list copied one workgroup per object (see kvm_batch_copy) is not
- * reserved here: it is allocated at that list's first such call, so a steady
- * state is allocation-free once each list has been copied twice.
+ * the scratch or has such buffers to free, and frees them.
  * max_seqs, the sequences per call, needs no memory and is only range-checked
  * (at most 2^20). Errors: KVM_EINVAL (negative sizes), KVM_ERANGE, KVM_ENOMEM,
  * KVM_EHIP. */
@@ -395,13 +392,9 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
  * found every object one piece, the call runs one workgroup per object with
  * no metadata pass (no scratch); an object that is not one piece then still
  * moves, and the shape goes back to the metadata pass at its next call.
- * Such a call takes the objects in destination order: a counting sort of the
- * list by destination runs on the stream at the list's first such call and is
- * kept in the context (4 bytes per object, allocated then; 128 lists, keyed
- * by the descriptor array's address, n_descs and the destination buffer; the
- * least recently used is replaced). Descriptors rewritten in place under the
- * same key keep the old order, which is still a permutation of the objects:
- * the result is the same, only the write order is no longer sorted.
+ * Objects are taken in list order: a list sorted by destination offset copies
+ * 1-4 % faster on MI355X (concurrent workgroups then write neighbouring
+ * objects), so a caller that builds its list on the host may sort it.
  * The first call with scratch on a second stream does not wait for the first
  * stream's copies (they left no events): it sets the scratch aside (allocated
  * until the next device synchronisation, see the waits convention above) and

@@ -55,13 +55,6 @@ constexpr int32_t kMergeWgsPerCu = 16;
 // ascending.
 constexpr int kOrderSlots = 16;
 
-// Destination orders of batched-copy lists copied one workgroup per object
-// (see kvm_batch_copy), keyed by the descriptor address, the object count and
-// the destination buffer: enough for a per-layer loop of up to 127 layers
-// plus its whole-sequence list. A stale order (descriptors rewritten in place)
-// is still a permutation of the list's objects, so results stay exact.
-constexpr int kCopyOrderSlots = 128;
-
 // The latest unpack or fused launch on one stream that read a slot's order.
 struct OrderReader {
     hipStream_t stream = nullptr;
@@ -163,7 +156,6 @@ struct kvm_ctx {
     hipStream_t copy_stream = nullptr;
     bool copy_pending = false;
     OrderSlot orders[kOrderSlots];
-    OrderSlot copy_orders[kCopyOrderSlots];
     uint64_t order_tick = 0;
     // Streams seen by calls that read a cached order, and by batch copies that
     // use the group scratch. While a context has seen one stream, stream order
@@ -341,46 +333,24 @@ int plan_seqs(const kvm_pool_layout* p, int32_t num_layers, const kvm_seq* seqs,
 
 void order_release(kvm_ctx* c)
 {
-    auto release = [c](OrderSlot& o) {
+    for (OrderSlot& o : c->orders) {
         dev_free(c, o.order, size_t(o.cap));
         if (o.ready) (void)hipEventDestroy(o.ready);
         for (OrderReader& r : o.readers) (void)hipEventDestroy(r.done);
         o = OrderSlot();
-    };
-    for (OrderSlot& o : c->orders) release(o);
-    for (OrderSlot& o : c->copy_orders) release(o);
+    }
     dev_free(c, c->d_count, size_t(c->count_cap));
     if (c->count_done) (void)hipEventDestroy(c->count_done);
     c->count_cap = 0;
     c->count_done = nullptr;
 }
 
-// The key of a cached order: up to three byte ranges, each a multiple of 8
-// bytes (for unpack: the pool's block count, then the batch's first tiles and
-// records; for a copy list: its descriptor address, count and destination
-// buffer). A lookup compares a 64-bit hash of the ranges first and their bytes
-// only where the hash matches; the key is built only when a slot stores it.
-struct OrderKey {
-    const void* p[3] = {nullptr, nullptr, nullptr};
-    size_t bytes[3] = {0, 0, 0};
-    int segs = 0;
-    void add(const void* q, size_t n)
-    {
-        p[segs] = q;
-        bytes[segs] = n;
-        ++segs;
-    }
-    size_t total() const { return bytes[0] + bytes[1] + bytes[2]; }
-};
-
-OrderKey unpack_key(const kvm::SeqBatch& b, const int64_t* num_blocks)
+// The key of an unpack order: the pool's block count, then the batch's first
+// tiles and records, byte for byte. A lookup compares a 64-bit hash of it
+// first and the bytes only where the hash matches; the key is never built.
+size_t key_bytes(const kvm::SeqBatch& b)
 {
-    static_assert(sizeof(kvm::SeqRec) % 8 == 0, "records hash as 64-bit words");
-    OrderKey k;
-    k.add(num_blocks, sizeof(int64_t));
-    k.add(b.tile0, sizeof(int64_t) * (size_t(b.n) + 1));
-    k.add(b.rec, sizeof(kvm::SeqRec) * size_t(b.n));
-    return k;
+    return sizeof(int64_t) * (size_t(b.n) + 2) + sizeof(kvm::SeqRec) * size_t(b.n);
 }
 
 uint64_t mix_words(uint64_t h, const void* p, size_t bytes)  // bytes: a multiple of 8
@@ -395,32 +365,31 @@ uint64_t mix_words(uint64_t h, const void* p, size_t bytes)  // bytes: a multipl
     return h;
 }
 
-uint64_t key_hash(const OrderKey& k)
+uint64_t order_hash(const kvm::SeqBatch& b, int64_t num_blocks)
 {
-    uint64_t h = 0x243F6A8885A308D3ull;
-    for (int i = 0; i < k.segs; ++i) h = mix_words(h, k.p[i], k.bytes[i]);
-    return h;
+    static_assert(sizeof(kvm::SeqRec) % 8 == 0, "records hash as 64-bit words");
+    uint64_t h = mix_words(0x243F6A8885A308D3ull, &num_blocks, sizeof(int64_t));
+    h = mix_words(h, b.tile0, sizeof(int64_t) * (size_t(b.n) + 1));
+    return mix_words(h, b.rec, sizeof(kvm::SeqRec) * size_t(b.n));
 }
 
-bool key_equals(const std::vector<char>& stored, const OrderKey& k)
+bool key_equals(const std::vector<char>& k, const kvm::SeqBatch& b, int64_t num_blocks)
 {
-    if (stored.size() != k.total()) return false;
-    const char* p = stored.data();
-    for (int i = 0; i < k.segs; ++i) {
-        if (std::memcmp(p, k.p[i], k.bytes[i]) != 0) return false;
-        p += k.bytes[i];
-    }
-    return true;
+    if (k.size() != key_bytes(b)) return false;
+    const char* p = k.data();
+    return std::memcmp(p, &num_blocks, sizeof(int64_t)) == 0 &&
+           std::memcmp(p + sizeof(int64_t), b.tile0, sizeof(int64_t) * (size_t(b.n) + 1)) == 0 &&
+           std::memcmp(p + sizeof(int64_t) * (size_t(b.n) + 2), b.rec,
+                       sizeof(kvm::SeqRec) * size_t(b.n)) == 0;
 }
 
-void key_store(std::vector<char>& stored, const OrderKey& k)
+void key_store(std::vector<char>& k, const kvm::SeqBatch& b, int64_t num_blocks)
 {
-    stored.resize(k.total());  // keeps its capacity
-    char* p = stored.data();
-    for (int i = 0; i < k.segs; ++i) {
-        std::memcpy(p, k.p[i], k.bytes[i]);
-        p += k.bytes[i];
-    }
+    k.resize(key_bytes(b));  // keeps its capacity
+    char* p = k.data();
+    std::memcpy(p, &num_blocks, sizeof(int64_t));
+    std::memcpy(p + sizeof(int64_t), b.tile0, sizeof(int64_t) * (size_t(b.n) + 1));
+    std::memcpy(p + sizeof(int64_t) * (size_t(b.n) + 2), b.rec, sizeof(kvm::SeqRec) * size_t(b.n));
 }
 
 // Before a call on `st` that reads a cached order or the batched-copy
@@ -432,13 +401,11 @@ void key_store(std::vector<char>& stored, const OrderKey& k)
 // from then on every call records events (see note_reader, kvm_batch_copy).
 void retire_order_scratch(kvm_ctx* c)
 {
-    for (OrderSlot* set : {c->orders, c->copy_orders})
-        for (int i = 0; i < (set == c->orders ? kOrderSlots : kCopyOrderSlots); ++i) {
-            OrderSlot& o = set[i];
-            dev_retire(c, o.order, size_t(o.cap));
-            o.cap = 0;
-            o.valid = false;
-        }
+    for (OrderSlot& o : c->orders) {
+        dev_retire(c, o.order, size_t(o.cap));
+        o.cap = 0;
+        o.valid = false;
+    }
     dev_retire(c, c->d_count, size_t(c->count_cap));
     c->count_cap = 0;
     c->count_pending = false;
@@ -501,21 +468,16 @@ int note_reader(kvm_ctx* c, OrderSlot* o, hipStream_t st)
     return KVM_OK;
 }
 
-// A cached order (one of `nslots` slots) for `key`, sorted on `st` by
-// launch(count_scratch, order) if it is not cached; `entries` is its length and
-// `count_words` the counting scratch its sort needs. Device memory is obtained
-// before anything is enqueued.
-template <class Launch>
-int cached_order(kvm_ctx* c, OrderSlot* slots, int nslots, const OrderKey& key, int64_t entries,
-                 int64_t count_words, const char* what, Launch&& launch, hipStream_t st,
+// The unpack order of batch b, sorting it on `st` if it is not cached.
+// Device memory is obtained before anything is enqueued for this batch.
+int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStream_t st,
                  OrderSlot** out)
 {
     enter_stream(c, &c->order_streams, st, retire_order_scratch);
-    const uint64_t hash = key_hash(key);
+    const uint64_t hash = order_hash(b, num_blocks);
     ++c->order_tick;
-    for (int i = 0; i < nslots; ++i) {
-        OrderSlot& o = slots[i];
-        if (o.valid && o.hash == hash && key_equals(o.key, key)) {
+    for (OrderSlot& o : c->orders) {
+        if (o.valid && o.hash == hash && key_equals(o.key, b, num_blocks)) {
             if (o.stream != st && o.ready_set) {
                 hipError_t e = hipStreamWaitEvent(st, o.ready, 0);
                 if (e != hipSuccess) return fail_hip(c, e, "hipStreamWaitEvent");
@@ -525,39 +487,41 @@ int cached_order(kvm_ctx* c, OrderSlot* slots, int nslots, const OrderKey& key, 
             return KVM_OK;
         }
     }
-    OrderSlot* o = &slots[0];
-    for (int i = 1; i < nslots; ++i)
-        if (slots[i].used < o->used) o = &slots[i];
+    OrderSlot* o = &c->orders[0];
+    for (OrderSlot& x : c->orders)
+        if (x.used < o->used) o = &x;
     if (o->valid) {  // its sort or launches reading it may still be in flight
         hipError_t e = o->ready_set ? hipEventSynchronize(o->ready) : hipSuccess;
         if (e == hipSuccess) e = wait_readers(*o);
         if (e != hipSuccess) return fail_hip(c, e, "hipEventSynchronize");
         o->valid = false;
     }
+    const int64_t ntiles = b.tile0[b.n];
     hipError_t e;
     if (!o->ready && (e = hipEventCreateWithFlags(&o->ready, hipEventDisableTiming)) != hipSuccess) {
         o->ready = nullptr;
         return fail_hip(c, e, "hipEventCreateWithFlags");
     }
-    if (o->cap < entries) {
+    if (o->cap < ntiles) {
         // launches on the order's own stream may still read the old array
         // (they recorded no events): retire it; sizes grow at least 2x
-        const int64_t cap = std::max(entries, 2 * o->cap);
+        const int64_t cap = std::max(ntiles, 2 * o->cap);
         dev_retire(c, o->order, size_t(o->cap));
         o->cap = 0;
         if (!dev_alloc(c, &o->order, size_t(cap))) {
-            c->last_error = std::string("hipMalloc: ") + what;
+            c->last_error = "hipMalloc: unpack order";
             return KVM_ENOMEM;
         }
         o->cap = cap;
     }
-    if (c->count_cap < count_words) {
-        const int64_t cap = std::max(count_words, 2 * c->count_cap);
+    const int64_t words = 2 * (num_blocks + 2);
+    if (c->count_cap < words) {
+        const int64_t cap = std::max(words, 2 * c->count_cap);
         dev_retire(c, c->d_count, size_t(c->count_cap));
         c->count_cap = 0;
         c->count_pending = false;
         if (!dev_alloc(c, &c->d_count, size_t(cap))) {
-            c->last_error = std::string("hipMalloc: ") + what + " scratch";
+            c->last_error = "hipMalloc: unpack order scratch";
             return KVM_ENOMEM;
         }
         c->count_cap = cap;
@@ -570,10 +534,10 @@ int cached_order(kvm_ctx* c, OrderSlot* slots, int nslots, const OrderKey& key, 
     if (c->count_pending && c->count_stream != st &&
         (e = hipStreamWaitEvent(st, c->count_done, 0)) != hipSuccess)
         return fail_hip(c, e, "hipStreamWaitEvent");
-    e = launch(c->d_count, o->order);
-    if (e != hipSuccess) return fail_hip(c, e, what);
-    // on one stream, stream order covers later readers and the next sort; the
-    // first call on a second stream set the first stream's orders aside
+    e = kvm::launch_unpack_order(b, num_blocks, c->d_count, o->order, st);
+    if (e != hipSuccess) return fail_hip(c, e, "unpack order launch");
+    // on one stream, stream order covers later readers and the next sort;
+    // the first call on a second stream waits for the device instead
     o->ready_set = c->order_streams.multi;
     if (c->order_streams.multi) {
         if ((e = hipEventRecord(o->ready, st)) != hipSuccess ||
@@ -582,26 +546,13 @@ int cached_order(kvm_ctx* c, OrderSlot* slots, int nslots, const OrderKey& key, 
         c->count_stream = st;
         c->count_pending = true;
     }
-    key_store(o->key, key);
+    key_store(o->key, b, num_blocks);
     o->hash = hash;
     o->stream = st;
     o->used = c->order_tick;
     o->valid = true;
     *out = o;
     return KVM_OK;
-}
-
-// The unpack order of batch b: its tiles by destination block.
-int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, const int64_t* num_blocks, hipStream_t st,
-                 OrderSlot** out)
-{
-    return cached_order(
-        c, c->orders, kOrderSlots, unpack_key(b, num_blocks), b.tile0[b.n], 2 * (*num_blocks + 2),
-        "unpack order",
-        [&](uint32_t* cnt, int32_t* order) {
-            return kvm::launch_unpack_order(b, *num_blocks, cnt, order, st);
-        },
-        st, out);
 }
 
 // The batched-copy scratch, grown to at least `words` (2x at least): the old
@@ -667,27 +618,6 @@ int64_t copy_grid(kvm_ctx* c, const CopyHintKey& key, bool use_pieces, uint64_t*
     int64_t grid = *each ? np : std::max<int64_t>(np, 2 * int64_t(c->num_cus));
     if (c->max_wgs > 0) grid = std::min<int64_t>(grid, c->max_wgs);
     return std::max<int64_t>(1, std::min(grid, kMaxCopyGrid));
-}
-
-// The destination order of a copy list copied one object per workgroup: a
-// counting sort of its objects by dst_off >> shift, with the shift chosen so
-// that the buffer holds at most 2^20 + 1 buckets (128 KiB ones up to 128 GiB).
-int copy_order(kvm_ctx* c, const kvm_copy_desc* descs, int64_t n, uint64_t dst_base,
-               uint64_t dst_bytes, hipStream_t st, OrderSlot** out)
-{
-    uint32_t shift = 17;
-    while ((dst_bytes >> shift) > (uint64_t(1) << 20)) ++shift;
-    const int64_t nb = int64_t(dst_bytes >> shift) + 1;  // keys 0..nb-1 in the buffer, nb past it
-    const uint64_t words[5] = {uint64_t(uintptr_t(descs)), uint64_t(n), dst_base, dst_bytes, shift};
-    OrderKey key;
-    key.add(words, sizeof(words));
-    return cached_order(
-        c, c->copy_orders, kCopyOrderSlots, key, n, 2 * (nb + 2), "copy order",
-        [&](uint32_t* cnt, int32_t* order) {
-            return kvm::launch_copy_order(reinterpret_cast<const kvm::CopyDesc*>(descs), n, shift,
-                                          nb, cnt, order, st);
-        },
-        st, out);
 }
 
 // ------------------------------------------------ precondition checks ---
@@ -1074,7 +1004,7 @@ static int pack_or_unpack(kvm_ctx* ctx, const kvm_pool_layout* layout, const voi
         for (size_t i = 0; i < batches.size(); ++i) {
             const int64_t ntiles = batches[i].tile0[batches[i].n];
             if (layout->num_blocks > 16 * ntiles + 65536) continue;
-            rc = unpack_order(ctx, batches[i], &layout->num_blocks, st, &orders[i]);
+            rc = unpack_order(ctx, batches[i], layout->num_blocks, st, &orders[i]);
             if (rc != KVM_OK) return rc;
         }
     }
@@ -1203,7 +1133,7 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
     OrderSlot* orders[kOrderSlots] = {};
     for (size_t i = 0; i < hit.size(); ++i) {
         if (layout->num_blocks > 16 * hit[i].tile0[hit[i].n] + 65536) continue;
-        rc = unpack_order(ctx, keys[i], &layout->num_blocks, st, &orders[i]);
+        rc = unpack_order(ctx, keys[i], layout->num_blocks, st, &orders[i]);
         if (rc != KVM_OK) return rc;
     }
     const PoolGeom g = geom_of(layout);
@@ -1254,16 +1184,6 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     a.grid = copy_grid(ctx, key, use_pieces, &a.hint, &a.each);
     // one group or one workgroup per object: no scratch
     const bool scratch = !one_group && !a.each;
-    // One workgroup per object: the workgroups take the objects in
-    // destination order, so that those running together write neighbouring
-    // objects (cached per list: one sort at its first such call).
-    OrderSlot* corder = nullptr;
-    if (a.each) {
-        const int rc = copy_order(ctx, descs, n_descs, uint64_t(uintptr_t(dst_base)), dst_bytes, st,
-                                  &corder);
-        if (rc != KVM_OK) return rc;
-        a.order = corder->order;
-    }
     if (scratch) {
         enter_stream(ctx, &ctx->copy_streams, st, retire_copy_scratch);
         const int rc = grow_copy(ctx, kvm::copy_group_words(n_descs) + 3 * piece_cap);
@@ -1286,10 +1206,6 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
     }
     e = kvm::launch_batch_copy(a, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "batch copy launch");
-    if (corder) {
-        const int rc = note_reader(ctx, corder, st);
-        if (rc != KVM_OK) return rc;
-    }
     if (!scratch || !ctx->copy_streams.multi) return KVM_OK;
     e = hipEventRecord(ctx->copy_done, st);
     if (e != hipSuccess) return fail_hip(ctx, e, "hipEventRecord");

@@ -1122,58 +1122,21 @@ __global__ __launch_bounds__(1024, 8) void k_bc_copy(const CopyDesc* __restrict_
     }
 }
 
-// ---------------------------------------- batched copy, destination order ---
-// A counting sort of a list's objects by destination bucket (dst_off >> shift;
-// an offset past the buckets takes key nb), for the one-object-per-workgroup
-// copy: the workgroups running together then write neighbouring objects.
-// Objects of one bucket come out in any order; whatever the descriptors hold,
-// the result is a permutation of [0, n). Measured on MI355X with lists sorted
-// by destination beforehand: +1.8 % on the 256,000-object restore list as one
-// call, +3.5 % as 64 per-layer calls.
-
-__device__ __forceinline__ int64_t copy_order_key(const CopyDesc& x, uint32_t shift, int64_t nb)
-{
-    return int64_t(min(x.dst_off >> shift, uint64_t(nb)));
-}
-
-__global__ __launch_bounds__(256) void k_copy_order_count(const CopyDesc* __restrict__ descs,
-                                                          int64_t n, uint32_t shift, int64_t nb,
-                                                          uint32_t* __restrict__ cnt)
-{
-    const int64_t k = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (k >= n) return;
-    atomicAdd(&cnt[copy_order_key(descs[k], shift, nb)], 1u);
-}
-
-__global__ __launch_bounds__(256) void k_copy_order_place(const CopyDesc* __restrict__ descs,
-                                                          int64_t n, uint32_t shift, int64_t nb,
-                                                          uint32_t* __restrict__ cursor,
-                                                          int32_t* __restrict__ order)
-{
-    const int64_t k = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (k >= n) return;
-    const uint32_t pos = atomicAdd(&cursor[copy_order_key(descs[k], shift, nb)], 1u);
-    order[pos] = int32_t(k);
-}
-
 // One workgroup per object, straight from the descriptors (no metadata
-// launch): workgroup b copies object order[b] (the list's destination order,
-// a permutation of [0, n)), or object b without an order. A big object (as split_object) is
+// launch): workgroup k copies object k. A big object (as split_object) is
 // copied piece by piece as copy_piece does; any other object byte by byte by
 // the whole workgroup. Correct for every list; it is the launch of choice
 // only when every object is one piece, which the previous call of the same
 // list shape reported (hint_word). An object that is not one piece clears the
 // hint, so that the next call of the shape takes the metadata path again.
 __global__ __launch_bounds__(1024, 8) void k_bc_each(const CopyDesc* __restrict__ descs, int64_t n,
-                                                     const int32_t* __restrict__ order,
                                                      const char* __restrict__ src,
                                                      uint64_t src_bytes, char* __restrict__ dst,
                                                      uint64_t dst_bytes, uint64_t* hint,
                                                      unsigned long long* err)
 {
-    if (int64_t(blockIdx.x) >= n) return;
-    const int64_t k = order ? int64_t(order[blockIdx.x]) : int64_t(blockIdx.x);
-    if (k < 0 || k >= n) return;  // never for a permutation of [0, n)
+    const int64_t k = blockIdx.x;
+    if (k >= n) return;
     const CopyDesc x = descs[k];
     const uint64_t len = object_bytes(x, src_bytes, dst_bytes);
     const ObjSplit sp = split_object(x, src, src_bytes, dst, dst_bytes, true);
@@ -1274,21 +1237,6 @@ hipError_t launch_pack(int unit, const PoolGeom& g, const char* pool, int32_t nu
     KVM_UNIT_SWITCH(unit, KVM_PACK)
 #undef KVM_PACK
 #undef KVM_PACK_BS
-    return hipGetLastError();
-}
-
-hipError_t launch_copy_order(const CopyDesc* descs, int64_t n, uint32_t shift, int64_t nb,
-                             uint32_t* count_scratch, int32_t* order, hipStream_t st)
-{
-    const int64_t keys = nb + 1;
-    uint32_t* cnt = count_scratch;
-    uint32_t* cursor = count_scratch + keys;
-    const dim3 grid(uint32_t((n + 255) / 256));
-    hipLaunchKernelGGL(k_order_zero, dim3(uint32_t(std::min<int64_t>((keys + 255) / 256, 4096))),
-                       dim3(256), 0, st, cnt, keys);
-    hipLaunchKernelGGL(k_copy_order_count, grid, dim3(256), 0, st, descs, n, shift, nb, cnt);
-    hipLaunchKernelGGL(k_exclusive_scan<uint32_t>, dim3(1), dim3(1024), 0, st, cnt, cursor, keys);
-    hipLaunchKernelGGL(k_copy_order_place, grid, dim3(256), 0, st, descs, n, shift, nb, cursor, order);
     return hipGetLastError();
 }
 
@@ -1414,8 +1362,8 @@ hipError_t launch_batch_copy(const BatchCopyArgs& a, hipStream_t st)
     const int64_t ng = (a.n + kDescGroup - 1) / kDescGroup;
     const dim3 grid(uint32_t(a.grid));
     if (a.each) {
-        hipLaunchKernelGGL(k_bc_each, grid, dim3(1024), 0, st, a.descs, a.n, a.order, a.src,
-                           a.src_bytes, a.dst, a.dst_bytes, a.hint, a.err);
+        hipLaunchKernelGGL(k_bc_each, grid, dim3(1024), 0, st, a.descs, a.n, a.src, a.src_bytes,
+                           a.dst, a.dst_bytes, a.hint, a.err);
         return hipGetLastError();
     }
     if (ng == 1) {

@@ -176,8 +176,6 @@ struct BatchCopyArgs {
     uint32_t use_pieces;   // 0: every object goes to the wavefront shares
     int64_t grid;          // 1024-thread workgroups of the copy launch
     bool each;             // one workgroup per object, no metadata launch (k_bc_each)
-    const int32_t* order = nullptr;  // with each: workgroup b copies object order[b]
-                                     // (a permutation of [0, n)), else object b
     uint64_t* hint;        // receives the list's piece count + 1 and kHintUniform
                            // (device-visible), or null
     unsigned long long* err;
@@ -195,12 +193,6 @@ hipError_t static_scratch(int device, uint64_t** out);
 // a.grid workgroups: workgroup b copies pieces b, b + grid, ..., then its
 // share of the other objects. With a.each: one launch, workgroup b copying
 // objects b, b + grid, ... whole.
-// A permutation of a copy list's n objects by destination: a counting sort on
-// dst_off >> shift over nb buckets (offsets past them share key nb). It uses
-// 2 * (nb + 2) words of count_scratch.
-hipError_t launch_copy_order(const CopyDesc* descs, int64_t n, uint32_t shift, int64_t nb,
-                             uint32_t* count_scratch, int32_t* order, hipStream_t st);
-
 hipError_t launch_batch_copy(const BatchCopyArgs& a, hipStream_t st);
 
 }  // namespace kvm

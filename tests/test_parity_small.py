@@ -157,108 +157,6 @@ def test_batch_copy_huge_objects(ctx, gpu, n):
                    np.full(arena, SENTINEL, np.uint8), d, label=f"huge objects n={n}")
 
 
-def _one_piece_list(seed, n, obj, arena):
-    lens = np.full(n, obj, np.int64)
-    return _descs(wl.placements(seed, 1, lens, arena), wl.placements(seed, 2, lens, arena), lens)
-
-
-def test_batch_copy_destination_order_stale_and_skipped(gpu):
-    """Lists of one-piece objects are copied one workgroup per object in a
-    destination order cached per descriptor array. Rewriting the array in place
-    (same address and count) leaves a stale order, which must still copy every
-    object of the new list; objects outside the buffer are skipped and counted."""
-    c = kv.Context(0)
-    try:
-        rng = np.random.default_rng(95)
-        arena, n, obj = 48 << 20, 300, 64 << 10
-        src_np = rng.integers(0, 256, arena, dtype=np.uint8)
-        src = up(src_np, gpu)
-        dst = up(np.full(arena, SENTINEL, np.uint8), gpu)
-        want = np.full(arena, SENTINEL, np.uint8)
-        a = _one_piece_list(95, n, obj, arena)
-        dd = up(a.view(np.uint8), gpu)
-        for call in range(3):                  # metadata pass, then one workgroup per object
-            kv.kvm_batch_copy(c.handle, dst, arena, src, arena, dd, n)
-            oracle.batch_copy(want, src_np, a)
-        torch.cuda.synchronize()
-        assert np.array_equal(down(dst), want), "list a"
-        b = _one_piece_list(96, n, obj, arena)
-        bad = [7, 150, 299]
-        b[bad, 1] = arena + np.array([0, 4096, 1 << 30], np.uint64)   # past the buffer
-        dd.copy_(torch.from_numpy(b.view(np.uint8).reshape(-1)).to(gpu))
-        for call in range(2):                  # the cached order is list a's
-            kv.kvm_batch_copy(c.handle, dst, arena, src, arena, dd, n)
-        ok = np.ones(n, bool)
-        ok[bad] = False
-        oracle.batch_copy(want, src_np, b[ok])
-        oracle.batch_copy(want, src_np, b[ok])
-        torch.cuda.synchronize()
-        assert np.array_equal(down(dst), want), "list b under list a's order"
-        assert c.take_device_errors() == 2 * len(bad)
-    finally:
-        c.close()
-
-
-def test_batch_copy_destination_order_eviction(gpu):
-    """More one-piece lists than the order cache holds (130 > 128), each copied
-    twice, then all of them again: evicted orders are re-sorted, results exact."""
-    c = kv.Context(0)
-    try:
-        rng = np.random.default_rng(97)
-        arena, n, obj = 8 << 20, 80, 32 << 10
-        src_np = rng.integers(0, 256, arena, dtype=np.uint8)
-        src = up(src_np, gpu)
-        dst = up(np.full(arena, SENTINEL, np.uint8), gpu)
-        want = np.full(arena, SENTINEL, np.uint8)
-        lists = [_one_piece_list(1000 + k, n, obj, arena) for k in range(130)]
-        dds = [up(d.view(np.uint8), gpu) for d in lists]
-        for rnd in range(2):
-            for d, dd in zip(lists, dds):
-                for _ in range(2):
-                    kv.kvm_batch_copy(c.handle, dst, arena, src, arena, dd, n)
-                    oracle.batch_copy(want, src_np, d)
-        torch.cuda.synchronize()
-        assert np.array_equal(down(dst), want)
-        assert c.take_device_errors() == 0
-    finally:
-        c.close()
-
-
-def test_batch_copy_destination_order_two_streams(gpu):
-    """One-piece lists alternating between two streams with no host sync: the
-    first call on the second stream sets the first stream's orders aside, and
-    later calls order themselves by the library's events."""
-    c = kv.Context(0)
-    try:
-        rng = np.random.default_rng(98)
-        arena, obj = 96 << 20, 128 << 10
-        src_np = rng.integers(0, 256, arena, dtype=np.uint8)
-        src = up(src_np, gpu)
-        dst = up(np.full(arena, SENTINEL, np.uint8), gpu)
-        region = arena // 3                      # list k writes only its own third
-        lists = []
-        for k in range(3):
-            lens = np.full(200, obj, np.int64)
-            d = _descs(wl.placements(99, 1 + k, lens, arena),
-                       k * region + wl.placements(99, 4 + k, lens, region), lens)
-            lists.append(d)
-        dds = [up(d.view(np.uint8), gpu) for d in lists]
-        want = np.full(arena, SENTINEL, np.uint8)
-        for d in lists:
-            oracle.batch_copy(want, src_np, d)
-        a, b = torch.cuda.Stream(), torch.cuda.Stream()
-        torch.cuda.synchronize()
-        for rnd in range(4):
-            for k, dd in enumerate(dds):
-                st = a if (rnd + k) % 2 == 0 else b
-                kv.kvm_batch_copy(c.handle, dst, arena, src, arena, dd, len(lists[k]), stream=st)
-        torch.cuda.synchronize()
-        assert np.array_equal(down(dst), want)
-        assert c.take_device_errors() == 0
-    finally:
-        c.close()
-
-
 def test_batch_copy_alignment_matrix(ctx, gpu):
     """Every (src % 16, dst % 16) pair, with lengths 0..300 and one 1 MiB object."""
     rng = np.random.default_rng(22)
