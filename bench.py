@@ -28,9 +28,9 @@ S+3 (the defaults are the workloads' own seeds).
 output of the layer loop, the MLA loop and the two copy lists on the device
 against the operations' definitions (no oracle: plain torch indexing).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S] [--verify] [--no-cpu]
-                      [--no-batch-copy] [--no-host] [--no-pipeline] [--no-mla]
-                      [--no-restore] [--no-small]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--seed S] [--verify]
+                      [--config c3,c4,c5] [--reps R] [--no-cpu] [--no-batch-copy]
+                      [--no-host] [--no-pipeline] [--no-mla] [--no-restore] [--no-small]
 """
 from __future__ import annotations
 
@@ -69,10 +69,27 @@ def parse():
     ap.add_argument("--no-small", action="store_true", help="skip the small-call section")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the layerwise overlap section (workgroup-bounded moves)")
+    ap.add_argument("--config", default="c3,c4,c5",
+                    help="comma list of the other workloads to run after the layer loop (C2, "
+                         "always run): c3 the restore list, c4 the MLA loop, c5 the small-object "
+                         "copy; 'none' for the layer loop alone")
+    ap.add_argument("--reps", type=int, default=0,
+                    help="timed repetitions of each copy list and of the MLA loops "
+                         "(0: 10 per copy list, 5 per MLA loop)")
     ap.add_argument("--verify", action="store_true",
                     help="after each timed section, check its outputs on the device against the "
                          "operations' defining properties (untimed; exits 1 on a mismatch)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    cfg = {c.strip().lower() for c in args.config.split(",") if c.strip()} - {"none"}
+    unknown = cfg - {"c3", "c4", "c5"}
+    if unknown:
+        ap.error(f"--config: unknown workload(s) {sorted(unknown)}; choose from c3, c4, c5")
+    args.no_restore |= "c3" not in cfg
+    args.no_mla |= "c4" not in cfg
+    args.no_batch_copy |= "c5" not in cfg
+    if args.reps < 0:
+        ap.error("--reps must be >= 0")
+    return args
 
 
 class Events:
@@ -1002,12 +1019,16 @@ def main():
     # Plain copies, for reference only: pack and the fused kernel move more than
     # either, so neither bounds the ops and no op is reported as a share of them.
     torch_copy, stream_copy = plain_copies(torch, kv, ctx, dev)
+    copy_reps, mla_reps = (args.reps, args.reps) if args.reps else (10, 5)
     mla = None if args.no_mla else run_verify(
-        lambda: mla_section(torch, kv, wl, ctx, dev, args.seed + 2, verify=args.verify))
+        lambda: mla_section(torch, kv, wl, ctx, dev, args.seed + 2, reps=mla_reps,
+                            verify=args.verify))
     bc = None if args.no_batch_copy else run_verify(
-        lambda: batch_copy_section(torch, kv, wl, ctx, dev, args.seed + 3, verify=args.verify))
+        lambda: batch_copy_section(torch, kv, wl, ctx, dev, args.seed + 3, reps=copy_reps,
+                                   verify=args.verify))
     restore = None if args.no_restore else run_verify(
-        lambda: restore_section(torch, kv, wl, ctx, dev, args.seed + 1, verify=args.verify))
+        lambda: restore_section(torch, kv, wl, ctx, dev, args.seed + 1, reps=copy_reps,
+                                verify=args.verify))
     if args.verify:
         for name, sec in (("mla_layer_loop", mla), ("batch_copy", bc),
                           ("batch_copy_restore", restore)):

@@ -101,3 +101,30 @@ def test_profile_commands_run_committed_files_with_known_flags():
                                     "--marker-trace", " -s ", " -r ")), cmd
             seen += 1
     assert seen >= 4
+
+
+def test_config_and_reps_flags():
+    """--config picks the workloads run after the layer loop (the --no-* flags
+    still apply), --reps sets the repetitions; unknown workloads are refused."""
+    b = _bench()
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        a = b.parse()
+        assert (a.no_restore, a.no_mla, a.no_batch_copy, a.reps) == (False, False, False, 0)
+        sys.argv = ["bench.py", "--config", "c3, C5", "--reps", "4"]
+        a = b.parse()
+        assert (a.no_restore, a.no_mla, a.no_batch_copy, a.reps) == (False, True, False, 4)
+        sys.argv = ["bench.py", "--config", "none", "--no-restore"]
+        a = b.parse()
+        assert a.no_restore and a.no_mla and a.no_batch_copy
+        for bad in (["--config", "c2"], ["--reps", "-1"]):
+            sys.argv = ["bench.py", *bad]
+            try:
+                b.parse()
+            except SystemExit as e:
+                assert e.code == 2
+            else:
+                raise AssertionError(f"{bad} accepted")
+    finally:
+        sys.argv = old
