@@ -35,7 +35,11 @@ constexpr int64_t kMaxDescs = int64_t(1) << 32;
 //    Llama layer loop (4 KiB rows, 16,640 tiles) the cap moves 6.7 % more
 //    than one workgroup per tile, with a much tighter spread; 32 or 48 KiB
 //    tiles change nothing. Pack and unpack lose under any cap, so they keep
-//    one workgroup per tile.
+//    one workgroup per tile. What holds merge there (5.6-6.2 TB/s) is the
+//    read of one layer of the Full Block, 4 KiB rows at a power-of-two
+//    128 KiB stride: with the same rows contiguous, or the stride padded by
+//    4 KiB, one workgroup per 128 KiB tile moves 6.0-6.1 TB/s, while on the
+//    strided slice no tile shape tried beats this one.
 //  - shorter rows: 50 KiB tiles (44 MLA rows of 1152 B) and one workgroup
 //    per tile. On the MLA loop: 6.31 TB/s, against 5.96 with 128 KiB tiles
 //    and 5.57 with 128 KiB tiles under the cap; with 1024-byte rows, or 32

@@ -620,8 +620,9 @@ __global__ __launch_bounds__(1024) void k_exclusive_scan(const T* __restrict__ i
 //     all multiples of 16 bytes) are cut into pieces of at most kPieceBytes,
 //     and each piece is copied by one 1024-thread workgroup with the whole
 //     piece in flight (8 vectors per thread, each wavefront 8 KiB of
-//     consecutive bytes), so that the workgroups running together cover a
-//     compact stretch of a few objects;
+//     consecutive bytes; 4 vectors and 4 KiB for pieces of at most 64 KiB),
+//     so that the workgroups running together cover a compact stretch of a
+//     few objects;
 //   - every other object (short, or with source and destination not equally
 //     aligned modulo 16) is copied by wavefronts that each take an equal share
 //     of those objects' bytes and walk them.
@@ -631,9 +632,10 @@ __global__ __launch_bounds__(1024) void k_exclusive_scan(const T* __restrict__ i
 // same from the 64 descriptors.
 //
 // Measured on MI355X against a wavefront-share copy of the whole list (the
-// earlier design here), all outputs identical: one 2 GiB object 5.2 -> 6.1-6.3
-// TB/s, 200,000 objects of 4-128 KiB 5.1 -> 5.7, the 256,000-object restore
-// list 6.0 -> 6.2 as one call and 5.2 -> 5.9 as 64 per-layer calls. A
+// earlier design here), in one process on two machines, all outputs
+// identical: one 2 GiB object 5.2-5.5 -> 5.9-6.0 TB/s, 200,000 objects of
+// 4-128 KiB 5.1 -> 5.7, the 256,000-object restore list 6.0-6.25 -> 6.2-6.25
+// as one call and 5.2-5.3 -> 5.4-5.9 as 64 per-layer calls. A
 // workgroup that loops over several pieces loses 5-10 %: its loads wait for
 // its own earlier stores (one counter for both), so the grid holds one
 // workgroup per piece where it can (see launch_batch_copy).
