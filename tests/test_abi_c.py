@@ -38,6 +38,8 @@ int main(void)
     if (kvm_merge_layer(NULL, 16, &mseq, 1, NULL) != KVM_EINVAL) return 7;
     if (kvm_unpack_merge_layer(NULL, &layout, NULL, 1, 0, &lseq, 1, NULL) != KVM_EINVAL) return 8;
     if (kvm_batch_copy(NULL, NULL, 0, NULL, 0, &desc, 1, NULL) != KVM_EINVAL) return 9;
+    if (kvm_batch_copy_noalloc(NULL, NULL, 0, NULL, 0, &desc, 1, NULL) != KVM_EINVAL) return 15;
+    if (KVM_NOALLOC_MAX_DESCS != (INT64_C(1) << 25) - 64) return 16;
     if (kvm_ctx_set_max_workgroups(NULL, 1) != KVM_EINVAL) return 10;
     if (kvm_ctx_set_checks(NULL, 1) != KVM_EINVAL) return 11;
     if (kvm_ctx_reserve_unpack(NULL, 1, 1) != KVM_EINVAL) return 13;

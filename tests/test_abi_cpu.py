@@ -68,6 +68,7 @@ def test_null_arguments_rejected_without_a_device():
     assert lib.kvm_pack_full(None, None, None, 1, None, 0, None) == kvmove.KVM_EINVAL
     assert lib.kvm_merge_layer(None, 16, None, 0, None) == kvmove.KVM_EINVAL
     assert lib.kvm_batch_copy(None, None, 0, None, 0, None, 0, None) == kvmove.KVM_EINVAL
+    assert lib.kvm_batch_copy_noalloc(None, None, 0, None, 0, None, 0, None) == kvmove.KVM_EINVAL
     assert lib.kvm_ctx_reserve(None, 1, 1) == kvmove.KVM_EINVAL
     assert lib.kvm_unpack_merge_layer(None, None, None, 1, 0, None, 0, None) == kvmove.KVM_EINVAL
     assert lib.kvm_ctx_set_max_workgroups(None, 4) == kvmove.KVM_EINVAL
