@@ -74,6 +74,7 @@
  *   - HIP graph capture of these calls is not supported: a captured unpack or
  *     fused launch refers to the context's cached tile order, which a later
  *     call with other block tables may overwrite before the graph replays.
+ *     kvm_batch_copy_noalloc is the exception (see there).
  *   - Caller preconditions: the block tables of one unpack or fused call
  *     hold no repeated entry; pool rows described by the layout do not overlap;
  *     copy destinations are pairwise disjoint and do not overlap the sources.
@@ -427,7 +428,12 @@ int kvm_batch_copy(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes, const void*
  *     GPU (on two streams, or from two threads) race and give an unspecified
  *     result. Order them on one stream, or synchronise between them;
  *   - the debug checks of kvm_ctx_set_checks are not applied.
- * The array's address is taken when the context is created (kvm_create). */
+ * The array's address is taken when the context is created (kvm_create).
+ * The call may be captured into a HIP graph: its launch configuration (the
+ * grid, or one workgroup per object) is fixed when it is captured, and every
+ * configuration copies any list of the captured length correctly, so a replay
+ * copies the descriptors as they are at that replay. Replays share the
+ * static array like any other call. */
 int kvm_batch_copy_noalloc(kvm_ctx* ctx, void* dst_base, uint64_t dst_bytes,
                            const void* src_base, uint64_t src_bytes,
                            const kvm_copy_desc* descs, int64_t n_descs, void* stream);

@@ -3,7 +3,8 @@
 The no-alloc entry point keeps its scratch in the device's static array; its
 output must equal the allocating entry point's, byte for byte, and the
 oracle's, on two calls in a row (the second with a smaller list), while the
-context's device memory stays where it was.
+context's device memory stays where it was. It is also replayed from a HIP
+graph capture, for the callers it is for.
 """
 
 import numpy as np
@@ -96,5 +97,61 @@ def test_noalloc_short_list_and_limits(gpu):
         assert lib.kvm_batch_copy_noalloc(ctx.handle, dst.data_ptr(), arena, src.data_ptr(), arena,
                                           dst.data_ptr(), 0, st) == kv.KVM_OK
         assert ctx.take_device_errors() == 0
+    finally:
+        ctx.close()
+
+
+def _graph_list(seed, lens, arena):
+    return np.stack([wl.placements(seed, 1, lens, arena), wl.placements(seed, 2, lens, arena),
+                     lens], axis=1).astype(np.uint64)
+
+
+@pytest.mark.parametrize("kind", ["short", "pieces"])
+def test_noalloc_in_a_graph(gpu, kind):
+    """Captured into a HIP graph: the call allocates nothing, records no event
+    and clears nothing with a memset, so the capture holds only its kernels.
+    The graph is replayed six times with eager work in between that rewrites
+    the source, the destination and the descriptors (same count); every
+    replay equals the oracle on the buffers as they are then."""
+    say(f"  no-alloc batched copy under graph capture ({kind})")
+    ctx = kv.Context(0)
+    try:
+        rng = np.random.default_rng(111)
+        arena, n = 32 << 20, 700
+        if kind == "short":
+            lens = 256 * rng.integers(1, 9, size=n).astype(np.int64)
+        else:
+            lens = 16384 * rng.integers(1, 9, size=n).astype(np.int64)   # 16-128 KiB
+            arena = 256 << 20
+        src = torch.empty(arena, dtype=torch.uint8, device=gpu)
+        dst = torch.empty(arena, dtype=torch.uint8, device=gpu)
+        descs = torch.empty(n * 24, dtype=torch.uint8, device=gpu)
+        lists = [_graph_list(120 + k, lens, arena) for k in range(3)]
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        descs.copy_(torch.from_numpy(lists[0].view(np.uint8).reshape(-1)))
+        # two eager calls first: the kernels are loaded before the capture, and
+        # the list shape's piece count is known, so a one-piece-per-object list
+        # is captured as one workgroup per object
+        for _ in range(2):
+            kv.kvm_batch_copy_noalloc(ctx.handle, dst, arena, src, arena, descs, n)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            kv.kvm_batch_copy_noalloc(ctx.handle, dst, arena, src, arena, descs, n,
+                                      stream=torch.cuda.current_stream())
+        for rep in range(6):
+            d = lists[rep % 3]
+            src_np = wl.random_bytes(200 + rep, 1, arena)
+            src.copy_(torch.from_numpy(src_np))                 # eager work between replays
+            dst.fill_(SENTINEL)
+            descs.copy_(torch.from_numpy(d.view(np.uint8).reshape(-1)))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            want = np.full(arena, SENTINEL, np.uint8)
+            oracle.batch_copy(want, src_np, d)
+            assert np.array_equal(down(dst), want), f"replay {rep}"
+        assert ctx.take_device_errors() == 0
+        del g
     finally:
         ctx.close()
