@@ -183,7 +183,9 @@ def _check_copies(src, dst, descs, sample, gaps=None):
 def test_qwen32b_object_restore(ctx, gpu):
     """One 128000-token sequence as 256000 K/V objects of 128 KiB scattered in a
     36 GiB staging arena, restored into the paged pool: one call of all
-    objects, then 64 per-layer calls of 4000."""
+    objects (its first call, which runs the metadata pass, and a later one,
+    which the list's known shape makes one workgroup per object, as the bench
+    times it), then 64 per-layer calls of 4000."""
     descs_np, bt, pool_bytes = wl.qwen32b_object_descs()
     n = len(descs_np)
     need_free(wl.QWEN32B_STAGING + pool_bytes + (1 << 30))
@@ -194,10 +196,15 @@ def test_qwen32b_object_restore(ctx, gpu):
     descs = torch.from_numpy(descs_np.view(np.uint8).reshape(-1)).to(gpu)
     rng = np.random.default_rng(3)
     sample = np.concatenate([[0, n - 1], rng.choice(n, 3000, replace=False)])
-    for mode in ("one call", "per layer"):
+    for mode in ("one call", "one call, shape known", "per layer"):
         pool = torch.full((pool_bytes,), SENTINEL, **u8)
-        if mode == "one call":
+        if mode.startswith("one call"):
             kv.kvm_batch_copy(ctx.handle, pool, pool_bytes, staging, wl.QWEN32B_STAGING, descs, n)
+            if mode == "one call, shape known":   # the first call above left the shape's count
+                torch.cuda.synchronize()
+                pool.fill_(SENTINEL)
+                kv.kvm_batch_copy(ctx.handle, pool, pool_bytes, staging, wl.QWEN32B_STAGING,
+                                  descs, n)
         else:
             per = n // wl.QWEN32B_SHAPE.layers
             for l in range(wl.QWEN32B_SHAPE.layers):
@@ -304,7 +311,9 @@ def test_mla_agentic_layer_loop(ctx, gpu, fused):
 
 
 def test_small_objects(ctx, gpu):
-    """200000 objects of 256*U{16..512} bytes between two 16 GiB arenas."""
+    """200000 objects of 256*U{16..512} bytes between two 16 GiB arenas: the
+    first call (grid guessed), then a later one with the grid sized from the
+    piece count the first left, as the bench times it; each checked whole."""
     w = wl.SMALL_OBJS
     descs_np = wl.small_object_descs(w)
     n = len(descs_np)
@@ -315,9 +324,6 @@ def test_small_objects(ctx, gpu):
     wl.fill_random_bytes_(src, w.seed, 1)
     dst = torch.full((w.dst_arena,), SENTINEL, **u8)
     descs = torch.from_numpy(descs_np.view(np.uint8).reshape(-1)).to(gpu)
-    kv.kvm_batch_copy(ctx.handle, dst, w.dst_arena, src, w.src_arena, descs, n)
-    torch.cuda.synchronize()
-    assert ctx.take_device_errors() == 0
     rng = np.random.default_rng(5)
     sample = np.concatenate([[0, n - 1], rng.choice(n, 3000, replace=False)])
     order = np.argsort(descs_np[:, 1])
@@ -325,10 +331,16 @@ def test_small_objects(ctx, gpu):
     starts = descs_np[order, 1]
     gaps = [(int(ends[i]), int(starts[i + 1])) for i in rng.choice(n - 1, 300, replace=False)
             if starts[i + 1] > ends[i]]
-    _check_copies(src, dst, descs_np, sample, gaps)
-    say("  checking every object and every uncovered granule")
-    _check_all_objects(src, dst, descs_np)
-    _check_untouched(dst, descs_np)
+    for call in ("first call", "piece count known"):
+        if call != "first call":
+            dst.fill_(SENTINEL)
+        kv.kvm_batch_copy(ctx.handle, dst, w.dst_arena, src, w.src_arena, descs, n)
+        torch.cuda.synchronize()
+        assert ctx.take_device_errors() == 0
+        say(f"  {call}: checking every object and every uncovered granule")
+        _check_copies(src, dst, descs_np, sample, gaps)
+        _check_all_objects(src, dst, descs_np)
+        _check_untouched(dst, descs_np)
     del src, dst, descs
     torch.cuda.empty_cache()
 
