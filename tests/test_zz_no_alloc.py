@@ -75,6 +75,44 @@ def test_noalloc_matches_batch_copy_on_two_calls(gpu):
         ctx.close()
 
 
+@pytest.mark.parametrize("n", [3000, 70000], ids=["meta", "three-pass"])
+def test_noalloc_pieces(gpu, n):
+    """Objects of 1 KiB to 384 KiB (one to three pieces, ragged last pieces, the
+    short ones to the wavefront shares): the piece records then live in the
+    static array. Two calls in a row, the second once the shape's piece count
+    is known; each equals kvm_batch_copy's output and the oracle's."""
+    rng = np.random.default_rng(3000 + n)
+    lens = 256 * rng.integers(16, 1537, size=n).astype(np.int64)       # 4 KiB - 384 KiB
+    if n > 10000:                                  # keep the arena near 1 GiB: mostly 1-16 KiB
+        short = np.ones(n, bool)
+        short[::50] = False
+        lens[short] = 256 * rng.integers(4, 65, size=int(short.sum()))
+    arena = int(lens.sum()) + (64 << 20)
+    descs = np.stack([wl.placements(3000 + n, 1, lens, arena), wl.placements(3000 + n, 2, lens, arena),
+                      lens], axis=1).astype(np.uint64)
+    ctx = kv.Context(0)
+    try:
+        src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+        src = up(src_np, gpu)
+        want = np.full(arena, SENTINEL, np.uint8)
+        oracle.batch_copy(want, src_np, descs)
+        for call in range(2):
+            say(f"  call {call}: {n} objects, {int(lens.sum()) >> 20} MiB")
+            dst_b = up(np.full(arena, SENTINEL, np.uint8), gpu)
+            before = ctx.device_bytes()
+            got_b = _copy("kvm_batch_copy_noalloc", ctx, src, dst_b, arena, descs, gpu)
+            assert ctx.device_bytes() == before, "the no-alloc call changed the context's memory"
+            del dst_b
+            dst_a = up(np.full(arena, SENTINEL, np.uint8), gpu)
+            got_a = _copy("kvm_batch_copy", ctx, src, dst_a, arena, descs, gpu)
+            del dst_a
+            assert np.array_equal(got_b, want), f"call {call}: no-alloc differs from the oracle"
+            assert np.array_equal(got_a, got_b), f"call {call}: no-alloc differs from kvm_batch_copy"
+        assert ctx.take_device_errors() == 0
+    finally:
+        ctx.close()
+
+
 def test_noalloc_short_list_and_limits(gpu):
     """A one-group list (at most 64 objects) and the length limit."""
     arena = 1 << 20
