@@ -3,7 +3,8 @@ oracle): random layers, sides (1-4), block sizes, row sizes (any byte count,
 so every move width), pool layouts, block and token-stride padding, base
 offsets, request counts and token counts, including empty requests; random
 merge row sizes and paddings; random copy lists with zero-length objects and
-arbitrary alignment. The oracle runs first in every runner, so a case that
+arbitrary alignment, and lists on 16-byte granules whose objects are cut into
+pieces, each copied twice. The oracle runs first in every runner, so a case that
 does not fit its buffers fails on the CPU before any kernel runs."""
 import os
 
@@ -86,3 +87,36 @@ def test_random_batch_copy(ctx, gpu, i):
     say(f"  random copy case {i}")
     run_batch_copy(ctx, gpu, r.integers(0, 256, src_size, dtype=np.uint8),
                    np.full(dst_size, SENTINEL, np.uint8), descs, label=f"random {i}")
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_random_batch_copy_pieces(ctx, gpu, i):
+    """Lists on 16-byte granules, objects up to 512 KiB (zero to four pieces,
+    ragged last pieces), with a share of unaligned, short and empty objects,
+    and sometimes nothing but one-piece objects; each list is copied twice, the
+    second call with the list's shape known (its grid from the piece count, or
+    one workgroup per object)."""
+    r = np.random.default_rng([2028, i])
+    n = int(r.integers(1, 400))
+    lens = 16 * r.integers(1, 32768, size=n)
+    uniform = r.random() < 0.3
+    if uniform:                                    # every object one piece
+        lens = 16 * r.integers(1024, 8193, size=n)
+    else:
+        odd = r.random(n) < 0.15
+        lens[odd] = r.integers(0, 70000, size=int(odd.sum()))       # any length, any size
+    slots = (lens + 15) // 16 * 16 + 16          # whole granules, room for a shifted source
+    dst_size = int(slots.sum()) + int(r.integers(0, 1 << 16)) + 16
+    src_size = int(slots.sum()) + int(r.integers(0, 1 << 16)) + 16
+    dst_off = wl.placements(7000 + i, 1, slots, dst_size, granule=16)
+    src_off = wl.placements(7000 + i, 2, slots, src_size, granule=16)
+    if not uniform:
+        shift = r.random(n) < 0.1
+        src_off[shift] += r.integers(1, 16, size=int(shift.sum()))   # unaligned sources
+    descs = np.stack([src_off.astype(np.uint64), dst_off.astype(np.uint64),
+                      lens.astype(np.uint64)], axis=1)
+    src_np = r.integers(0, 256, src_size, dtype=np.uint8)
+    say(f"  random piece copy case {i} ({n} objects{', one piece each' if uniform else ''})")
+    for call in range(2):
+        run_batch_copy(ctx, gpu, src_np, np.full(dst_size, SENTINEL, np.uint8), descs,
+                       label=f"random pieces {i} call {call}")
