@@ -46,16 +46,25 @@ def test_interleaved_streams(gpu, seed):
     want_pool = np.full(L * S * N * B * rb, SENTINEL, np.uint8)
     want_out = [[None] * L for _ in range(SETS)]
 
-    # copy lists: each writes its own region of dst (multi-group, so they use the scratch)
-    CP, region = 6, 1 << 19
-    src_np = rng.integers(0, 256, 1 << 20, dtype=np.uint8)
+    # copy lists, each writing its own region of dst, all of more than 64 objects:
+    # short objects (wavefront shares, with scratch), one-piece objects (one
+    # workgroup per object once the list's shape is known) and objects of up to
+    # two pieces (piece records in the scratch)
+    CP, region, src_bytes = 6, 1 << 25, 1 << 26
+    src_np = rng.integers(0, 256, src_bytes, dtype=np.uint8)
     src = up(src_np, gpu)
     dst = up(np.full(CP * region, SENTINEL, np.uint8), gpu)
     want_dst = np.full(CP * region, SENTINEL, np.uint8)
     lists, dlists = [], []
     for k in range(CP):
-        lens = 256 * rng.integers(1, 4, size=int(rng.integers(65, 400)))
-        d = np.stack([wl.placements(700 + k, seed, lens, 1 << 20),
+        n = int(rng.integers(65, 120))
+        if k % 3 == 0:
+            lens = 256 * rng.integers(1, 4, size=n)
+        elif k % 3 == 1:
+            lens = 16384 * rng.integers(1, 9, size=n)          # 16-128 KiB, one piece
+        else:
+            lens = 4096 * rng.integers(4, 65, size=n)          # 16-256 KiB, up to two pieces
+        d = np.stack([wl.placements(700 + k, seed, lens, src_bytes),
                       k * region + wl.placements(710 + k, seed, lens, region), lens],
                      axis=1).astype(np.uint64)
         lists.append(d)
@@ -87,7 +96,7 @@ def test_interleaved_streams(gpu, seed):
                 oracle.merge_layer(C, fb_np[k][l * C:], L * C, T, miss_np[k], C, 8, o, C)
                 want_out[k][l] = o
             else:
-                kv.kvm_batch_copy(c.handle, dst, CP * region, src, 1 << 20, dlists[ck],
+                kv.kvm_batch_copy(c.handle, dst, CP * region, src, src_bytes, dlists[ck],
                                   len(lists[ck]), stream=st)
                 oracle.batch_copy(want_dst, src_np, lists[ck])
         c.set_max_workgroups(0)
