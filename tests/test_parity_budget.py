@@ -91,6 +91,25 @@ def test_budget_batch_copy(budget_ctx, gpu):
 
 
 @pytest.mark.parametrize("budget_ctx", BUDGETS, indirect=True)
+@pytest.mark.parametrize("kind", ["one-piece", "multi-piece"])
+def test_budget_batch_copy_pieces(budget_ctx, gpu, kind):
+    """Aligned objects cut into pieces (16-128 KiB: one piece each; 16-512 KiB:
+    up to four), so that a budgeted grid walks several pieces per workgroup;
+    each list copied twice, the second time with its shape known (one
+    workgroup per object only where the budget allows a grid that large)."""
+    rng = np.random.default_rng(79 if kind == "one-piece" else 80)
+    hi = 8 if kind == "one-piece" else 32
+    lens = 16384 * rng.integers(1, hi + 1, size=300)
+    arena = int(lens.sum()) + (8 << 20)
+    descs = np.stack([wl.placements(79, 1, lens, arena), wl.placements(79, 2, lens, arena),
+                      lens], axis=1).astype(np.uint64)
+    src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+    for call in range(2):
+        run_batch_copy(budget_ctx, gpu, src_np, np.full(arena, SENTINEL, np.uint8), descs,
+                       label=f"{kind}, budget, call {call}")
+
+
+@pytest.mark.parametrize("budget_ctx", BUDGETS, indirect=True)
 def test_budget_batch_copy_short_list(budget_ctx, gpu):
     """40 objects (one launch, shares found by each wavefront's own scan), one
     of them 4 MiB so that it spans many shares, and one out of range."""
