@@ -317,13 +317,32 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
     def pack_host():
         kv.kvm_pack_full(ctx.handle, s["layout"], s["pool"], L, [kv.seq(bts[0], host_packed, t_all)])
 
+    # one layer of a restore from a host-DRAM staging buffer: 4,000 K/V objects
+    # of 128 KiB packed in pinned host memory, copied by kvm_batch_copy into
+    # 4,000 shuffled 128 KiB slots of a device buffer (the restore list's
+    # per-layer call, from host memory)
+    import numpy as np
+    nobj, obj = 4000, 128 << 10
+    host_stage = torch.empty(nobj * obj, dtype=torch.uint8, pin_memory=True)
+    dev_slots = torch.empty(nobj * obj, dtype=torch.uint8, device=fbs[0].device)
+    perm = np.random.default_rng(1234).permutation(nobj).astype(np.uint64)
+    d = np.stack([np.arange(nobj, dtype=np.uint64) * obj, perm * obj,
+                  np.full(nobj, obj, np.uint64)], axis=1)
+    host_descs = torch.from_numpy(d.view(np.uint8).reshape(-1)).to(fbs[0].device)
+
+    def restore_from_host():
+        kv.kvm_batch_copy(ctx.handle, dev_slots, nobj * obj, host_stage, nobj * obj,
+                          host_descs, nobj)
+
     unpack_loop()
     merge_loop()
     pack_host()
+    restore_from_host()
     for _ in range(reps):
         ev.around("h2d_unpack", unpack_loop)
         ev.around("d2h_merge", merge_loop)
         ev.around("d2h_pack", pack_host)
+        ev.around("h2d_restore", restore_from_host)
         ev.around("h2d_copy", lambda: dev_buf.copy_(host_buf, non_blocking=True))
         ev.around("d2h_copy", lambda: host_buf.copy_(dev_buf, non_blocking=True))
     torch.cuda.synchronize()
@@ -332,7 +351,8 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
     h2d = (1 << 30) / (ev.mean_ms("h2d_copy") * 1e6)
     d2h = (1 << 30) / (ev.mean_ms("d2h_copy") * 1e6)
     pk_gbs = t_all * L * C / (ev.mean_ms("d2h_pack") * 1e6)
-    del host_fb, host_out, host_packed, dev_buf, host_buf
+    rs_gbs = nobj * obj / (ev.mean_ms("h2d_restore") * 1e6)
+    del host_fb, host_out, host_packed, dev_buf, host_buf, host_stage, dev_slots, host_descs
     return {"workload": "request 0 of the layer loop, Full Block / complete_layer in pinned host memory",
             "unpack_layer_from_host": {"pcie_bytes_per_launch": t_hit * C,
                                        "ms_per_launch": round(ev.mean_ms("h2d_unpack") / L, 3),
@@ -349,6 +369,12 @@ def host_tier_section(torch, kv, ctx, s, reps=3):
                                     "pcie_GBps": round(pk_gbs, 1),
                                     "frac_of_d2h_copy": round(pk_gbs / d2h, 3),
                                     "frac_of_pcie_peak": round(pk_gbs / PCIE_PEAK_GBS, 3)},
+            "batch_copy_restore_layer_from_host": {"objects": nobj, "object_bytes": obj,
+                                                   "pcie_bytes_per_call": nobj * obj,
+                                                   "ms_per_call": round(ev.mean_ms("h2d_restore"), 3),
+                                                   "pcie_GBps": round(rs_gbs, 1),
+                                                   "frac_of_h2d_copy": round(rs_gbs / h2d, 3),
+                                                   "frac_of_pcie_peak": round(rs_gbs / PCIE_PEAK_GBS, 3)},
             "torch_pinned_copy_GBps": {"h2d": round(h2d, 1), "d2h": round(d2h, 1)},
             "pcie_peak_GBps_per_direction": PCIE_PEAK_GBS}
 

@@ -33,7 +33,9 @@
  *   - Device pointers are HIP device addresses on the context's device. A Full
  *     Block, miss rows or complete_layer may also live in pinned host memory
  *     (hipHostMalloc): the kernels then read or write it over PCIe through its
- *     device-visible address (DualPath's host-DRAM prompt buffers). Host
+ *     device-visible address (DualPath's host-DRAM prompt buffers). So may a
+ *     batched copy's source or destination buffer (a restore from a host-DRAM
+ *     staging buffer); its descriptor array stays in device memory. Host
  *     arrays (kvm_seq, kvm_merge_seq) are read during the call and may be
  *     reused as soon as it returns: their contents travel to the kernels as
  *     kernel arguments, up to 128 records per launch.

@@ -94,3 +94,38 @@ def test_host_full_block(ctx, gpu, L, S, N, B, rb, reqs):
                     f"merge into host, layer {layer}, request {i}, fused={fused}"
         pool_after = want_pool.copy()
     assert ctx.take_device_errors() == 0
+
+
+@pytest.mark.parametrize("direction", ["host-to-device", "device-to-host"])
+@pytest.mark.parametrize("kind", ["pieces", "short"])
+def test_host_batch_copy(ctx, gpu, direction, kind):
+    """The batched copy with its source (a restore from a host-DRAM staging
+    buffer) or its destination in pinned host memory; the descriptors stay in
+    device memory. Each list copied twice (the second time with its shape
+    known), every byte against the oracle."""
+    rng = np.random.default_rng(41 if kind == "pieces" else 42)
+    n = 600
+    lens = (16384 * rng.integers(1, 17, size=n) if kind == "pieces"
+            else 256 * rng.integers(1, 9, size=n)).astype(np.int64)
+    arena = int(lens.sum()) + (4 << 20)
+    descs = np.stack([wl.placements(43, 1, lens, arena), wl.placements(43, 2, lens, arena),
+                      lens], axis=1).astype(np.uint64)
+    say(f"  host batch copy {direction} {kind}: {n} objects, {int(lens.sum()) >> 20} MiB")
+    src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+    want = np.full(arena, SENTINEL, np.uint8)
+    oracle.batch_copy(want, src_np, descs)
+    dd = up(descs.view(np.uint8), gpu)
+    if direction == "host-to-device":
+        src = pinned(src_np)
+    else:
+        src = up(src_np, gpu)
+    for call in range(2):
+        if direction == "host-to-device":
+            dst = up(np.full(arena, SENTINEL, np.uint8), gpu)
+        else:
+            dst = pinned(np.full(arena, SENTINEL, np.uint8))
+        kv.kvm_batch_copy(ctx.handle, dst, arena, src, arena, dd, n)
+        torch.cuda.synchronize()
+        got = down(dst) if direction == "host-to-device" else dst.numpy()
+        assert np.array_equal(got, want), f"call {call}"
+    assert ctx.take_device_errors() == 0
