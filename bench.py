@@ -504,6 +504,7 @@ def plain_copies(torch, kv, ctx, dev, nbytes=2 << 30, reps=10):
     def rate(fn):
         for _ in range(2):
             fn()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):

@@ -576,6 +576,22 @@ int grow_copy(kvm_ctx* c, int64_t words)
     return KVM_OK;
 }
 
+// Pieces to size a grid for before the shape's count is known: one per object
+// (at most kPieceGuess); for a list of one object, as many as the smaller
+// buffer holds. One object can fill its buffers, and calls issued back to back
+// reach the device before the first has left its count: a 2 GiB object at the
+// one-per-object guess (a grid of 2 workgroups per CU, each looping over 32
+// pieces) moved 5.5 TB/s on MI355X against 6.1 at one workgroup per piece.
+int64_t first_guess(const CopyHintKey& key)
+{
+    if (key.n == 1) {
+        const uint64_t room = std::min(key.src_bytes, key.dst_bytes);
+        return int64_t(std::min<uint64_t>((room + kvm::kPieceBytes - 1) / kvm::kPieceBytes,
+                                          uint64_t(kPieceGuess)));
+    }
+    return std::min<int64_t>(key.n, kPieceGuess);
+}
+
 // Grid of a batched copy: one workgroup per piece of the list's big objects
 // (at least 2 per CU, which the wavefront shares of the other objects need),
 // within the workgroup budget. The piece count is known only on the device;
@@ -616,7 +632,7 @@ int64_t copy_grid(kvm_ctx* c, const CopyHintKey& key, bool use_pieces, uint64_t*
             *each = true;
             np = key.n;
         } else {
-            np = v ? int64_t((v & ~kvm::kHintUniform) - 1) : std::min<int64_t>(key.n, kPieceGuess);
+            np = v ? int64_t((v & ~kvm::kHintUniform) - 1) : first_guess(key);
         }
     }
     int64_t grid = *each ? np : std::max<int64_t>(np, 2 * int64_t(c->num_cus));

@@ -186,6 +186,43 @@ def test_batch_copy_one_large_object(ctx, gpu):
     run_batch_copy(ctx, gpu, src, np.full(n + 512, SENTINEL, np.uint8), d, label="one large")
 
 
+ONE_OBJECT_CASES = {
+    # (source offset, destination offset, length, source bytes, workgroup budget)
+    "pieces+ragged": (4096, 256, 5 * (128 << 10) + 4080, 6 << 20, 0),
+    "one-piece": (0, 1 << 20, 128 << 10, 2 << 20, 0),
+    "short-piece": (16, 32, (48 << 10) + 16, 1 << 20, 0),
+    "below-16KiB": (64, 128, (16 << 10) - 16, 1 << 20, 0),
+    "unaligned-big": (8, 3, (3 << 20) + 5, 4 << 20, 0),
+    "empty": (100, 200, 0, 1 << 20, 0),
+    "past-source-end": ((1 << 20) - 64, 0, 128, 1 << 20, 0),
+    "budget-3": (4096, 256, 40 * (128 << 10) + 512, 6 << 20, 3),
+}
+
+
+@pytest.mark.parametrize("case", list(ONE_OBJECT_CASES))
+def test_batch_copy_one_object(gpu, case):
+    """A list of one object (its own launch): full pieces, a ragged last piece,
+    a piece-sized and a sub-piece object, an object just under the 16 KiB
+    piece threshold, an unaligned big object (wavefront shares), an empty one,
+    one outside the source (skipped and counted) and a workgroup budget below
+    the piece count. Each list is copied twice: the second call sizes its grid
+    from the piece count the first one left."""
+    so, do, ln, sb, budget = ONE_OBJECT_CASES[case]
+    rng = np.random.default_rng(2900 + len(case))
+    src_np = rng.integers(0, 256, sb, dtype=np.uint8)
+    db = max(do + ln, 1 << 16) + 4096
+    d = _descs([so], [do], [ln])
+    bad = 1 if so + ln > sb else 0
+    c = kv.Context(0)
+    try:
+        c.set_max_workgroups(budget)
+        for call in range(2):
+            run_batch_copy(c, gpu, src_np, np.full(db, SENTINEL, np.uint8), d, expect_skipped=bad,
+                           label=f"one object {case} call {call}")
+    finally:
+        c.close()
+
+
 def test_batch_copy_many_tiny_objects(ctx, gpu):
     rng = np.random.default_rng(24)
     lens = rng.integers(0, 65, size=100000)
