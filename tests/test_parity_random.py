@@ -120,3 +120,42 @@ def test_random_batch_copy_pieces(ctx, gpu, i):
     for call in range(2):
         run_batch_copy(ctx, gpu, src_np, np.full(dst_size, SENTINEL, np.uint8), descs,
                        label=f"random pieces {i} call {call}")
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_random_batch_copy_one_object(gpu, i):
+    """Lists of one object: lengths from 0 to 2 MiB (none to 16 pieces, ragged
+    last pieces, often on 16-byte granules, sometimes any length), sources and
+    destinations at any alignment inside buffers of random size, sometimes an
+    object past a buffer's end (skipped and counted), and workgroup budgets
+    from none to below the piece count. Each list is copied twice: the first
+    call sizes its grid from the buffers, the second from the piece count the
+    first left."""
+    r = np.random.default_rng([2029, i])
+    ln = int(16 * r.integers(0, 131073)) if r.random() < 0.7 else int(r.integers(0, 1 << 21))
+    src_size = ln + int(r.integers(1, 1 << 20))
+    dst_size = ln + int(r.integers(1, 1 << 20))
+    so = int(r.integers(0, src_size - ln + 1))
+    do = int(r.integers(0, dst_size - ln + 1))
+    if r.random() < 0.4:                            # both 16-byte aligned
+        so, do = so // 16 * 16, do // 16 * 16
+    bad = 0
+    if r.random() < 0.1:                            # past the end of one buffer
+        if r.random() < 0.5:
+            so = src_size - max(ln, 1) + int(r.integers(1, 64))
+        else:
+            do = dst_size - max(ln, 1) + int(r.integers(1, 64))
+        ln = max(ln, 1)
+        bad = 1
+    budget = int(r.choice([0, 0, 0, 1, 3, 7, 64]))
+    descs = np.array([[so, do, ln]], np.uint64)
+    src_np = r.integers(0, 256, src_size, dtype=np.uint8)
+    say(f"  random one-object copy case {i}: {ln} B, src+{so % 16} dst+{do % 16}, budget {budget}")
+    c = kv.Context(0)
+    try:
+        c.set_max_workgroups(budget)
+        for call in range(2):
+            run_batch_copy(c, gpu, src_np, np.full(dst_size, SENTINEL, np.uint8), descs,
+                           expect_skipped=bad, label=f"random one object {i} call {call}")
+    finally:
+        c.close()
