@@ -390,11 +390,13 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
  * device: the metadata pass leaves it in pinned host memory under the call's
  * list shape (n_descs and the two buffers, address and size), and the next
  * call of that shape sizes its grid from it without waiting for the device;
- * the first call of a shape guesses, and then loops over the pieces its grid
- * does not hold (same result, slower). When the previous call of the shape
- * found every object one piece, the call runs one workgroup per object with
- * no metadata pass (no scratch); an object that is not one piece then still
- * moves, and the shape goes back to the metadata pass at its next call.
+ * the first call of a shape guesses (one piece per object; for a list of one
+ * object, as many pieces as the smaller buffer holds), and then loops over
+ * the pieces its grid does not hold (same result, slower). When the previous
+ * call of the shape found every object one piece, the call runs one
+ * workgroup per object with no metadata pass (no scratch); an object that is
+ * not one piece then still moves, and the shape goes back to the metadata
+ * pass at its next call.
  * Objects are taken in list order: a list sorted by destination offset copies
  * 1-4 % faster on MI355X (concurrent workgroups then write neighbouring
  * objects), so a caller that builds its list on the host may sort it.

@@ -166,7 +166,8 @@ struct kvm_ctx {
     // alone keeps a buffer from being rewritten under a launch that reads it,
     // so no event is recorded per call: each such record left the GPU idle
     // about 6 us between launches on MI355X. The first call on a second stream
-    // waits for the device once; from then on every call records its event.
+    // retires the buffers the first stream's launches may read (enter_stream)
+    // instead of waiting; from then on every call records its event.
     SingleStream order_streams;
     SingleStream copy_streams;
     uint32_t* d_count = nullptr;   // counting-sort scratch, 2 * (blocks + 2) words
@@ -541,7 +542,8 @@ int unpack_order(kvm_ctx* c, const kvm::SeqBatch& b, int64_t num_blocks, hipStre
     e = kvm::launch_unpack_order(b, num_blocks, c->d_count, o->order, st);
     if (e != hipSuccess) return fail_hip(c, e, "unpack order launch");
     // on one stream, stream order covers later readers and the next sort;
-    // the first call on a second stream waits for the device instead
+    // the first call on a second stream retires the arrays instead
+    // (enter_stream)
     o->ready_set = c->order_streams.multi;
     if (c->order_streams.multi) {
         if ((e = hipEventRecord(o->ready, st)) != hipSuccess ||

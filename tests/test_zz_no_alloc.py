@@ -139,6 +139,34 @@ def test_noalloc_short_list_and_limits(gpu):
         ctx.close()
 
 
+def test_noalloc_one_object(gpu):
+    """A list of one object (full pieces and a ragged last one; then a shorter
+    one): no scratch at all, the same bytes as kvm_batch_copy and the oracle,
+    on two calls in a row."""
+    arena = 8 << 20
+    ctx = kv.Context(0)
+    try:
+        rng = np.random.default_rng(31)
+        src_np = rng.integers(0, 256, arena, dtype=np.uint8)
+        src = up(src_np, gpu)
+        for call, ln in enumerate((5 * (128 << 10) + 4080, (48 << 10) + 16)):
+            descs = np.array([[4096, 512, ln]], np.uint64)
+            say(f"  call {call}: one object of {ln} bytes")
+            before = ctx.device_bytes()
+            got_b = _copy("kvm_batch_copy_noalloc", ctx, src, up(np.full(arena, SENTINEL, np.uint8), gpu),
+                          arena, descs, gpu)
+            assert ctx.device_bytes() == before, "the no-alloc call changed the context's memory"
+            got_a = _copy("kvm_batch_copy", ctx, src, up(np.full(arena, SENTINEL, np.uint8), gpu),
+                          arena, descs, gpu)
+            want = np.full(arena, SENTINEL, np.uint8)
+            oracle.batch_copy(want, src_np, descs)
+            assert np.array_equal(got_b, want), f"call {call}: no-alloc differs from the oracle"
+            assert np.array_equal(got_a, got_b), f"call {call}: no-alloc differs from kvm_batch_copy"
+        assert ctx.take_device_errors() == 0
+    finally:
+        ctx.close()
+
+
 def _graph_list(seed, lens, arena):
     return np.stack([wl.placements(seed, 1, lens, arena), wl.placements(seed, 2, lens, arena),
                      lens], axis=1).astype(np.uint64)
