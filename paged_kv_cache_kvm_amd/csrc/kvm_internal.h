@@ -191,8 +191,9 @@ hipError_t static_scratch(int device, uint64_t** out);
 
 // Metadata launches (none for a list of one group), then the copy launch of
 // a.grid workgroups: workgroup b copies pieces b, b + grid, ..., then its
-// share of the other objects. With a.each: one launch, workgroup b copying
-// objects b, b + grid, ... whole.
+// share of the other objects. A list of one object: one launch of its own, no
+// metadata. With a.each: one launch, workgroup b copying object b whole (the
+// grid then holds every object).
 hipError_t launch_batch_copy(const BatchCopyArgs& a, hipStream_t st);
 
 }  // namespace kvm
