@@ -172,7 +172,7 @@ def _graph_list(seed, lens, arena):
                      lens], axis=1).astype(np.uint64)
 
 
-@pytest.mark.parametrize("kind", ["short", "pieces"])
+@pytest.mark.parametrize("kind", ["short", "pieces", "one"])
 def test_noalloc_in_a_graph(gpu, kind):
     """Captured into a HIP graph: the call allocates nothing, records no event
     and clears nothing with a memset, so the capture holds only its kernels.
@@ -186,6 +186,9 @@ def test_noalloc_in_a_graph(gpu, kind):
         arena, n = 32 << 20, 700
         if kind == "short":
             lens = 256 * rng.integers(1, 9, size=n).astype(np.int64)
+        elif kind == "one":                      # one object: 24 full pieces and a ragged one
+            n = 1
+            lens = np.array([24 * (128 << 10) + 3840], np.int64)
         else:
             lens = 16384 * rng.integers(1, 9, size=n).astype(np.int64)   # 16-128 KiB
             arena = 256 << 20
