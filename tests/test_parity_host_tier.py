@@ -97,16 +97,19 @@ def test_host_full_block(ctx, gpu, L, S, N, B, rb, reqs):
 
 
 @pytest.mark.parametrize("direction", ["host-to-device", "device-to-host"])
-@pytest.mark.parametrize("kind", ["pieces", "short"])
+@pytest.mark.parametrize("kind", ["pieces", "short", "one"])
 def test_host_batch_copy(ctx, gpu, direction, kind):
     """The batched copy with its source (a restore from a host-DRAM staging
     buffer) or its destination in pinned host memory; the descriptors stay in
     device memory. Each list copied twice (the second time with its shape
     known), every byte against the oracle."""
-    rng = np.random.default_rng(41 if kind == "pieces" else 42)
-    n = 600
-    lens = (16384 * rng.integers(1, 17, size=n) if kind == "pieces"
-            else 256 * rng.integers(1, 9, size=n)).astype(np.int64)
+    rng = np.random.default_rng({"pieces": 41, "short": 42, "one": 44}[kind])
+    n = 1 if kind == "one" else 600
+    if kind == "one":                           # 40 full pieces and a ragged last one
+        lens = np.array([40 * (128 << 10) + 3840], np.int64)
+    else:
+        lens = (16384 * rng.integers(1, 17, size=n) if kind == "pieces"
+                else 256 * rng.integers(1, 9, size=n)).astype(np.int64)
     arena = int(lens.sum()) + (4 << 20)
     descs = np.stack([wl.placements(43, 1, lens, arena), wl.placements(43, 2, lens, arena),
                       lens], axis=1).astype(np.uint64)
