@@ -362,8 +362,11 @@ typedef struct {
  * {hit = full + layer*num_sides*row_bytes, hit_stride = token_stride (dense if
  * 0), t_hit, miss, miss_stride, t_miss, out, out_stride}, but each hit row is
  * read once: 3*H + 2*M bytes move instead of 4*H + 2*M. Launches: one fused
- * kernel per 128 requests for the hit rows (tiles in destination-block order,
- * as kvm_unpack_layer) and one for the miss rows.
+ * kernel per 128 requests with hit rows: their tiles (in destination-block
+ * order, as kvm_unpack_layer), then their miss rows as its last work items.
+ * Miss rows of requests with no hit rows, or whose miss address or stride
+ * would force narrower moves on the hit rows, take one merge launch of their
+ * own.
  * Errors: the union of kvm_unpack_layer's and kvm_merge_layer's (KVM_ECHECK
  * included). */
 int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* pool,

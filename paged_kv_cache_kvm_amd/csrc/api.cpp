@@ -1094,12 +1094,7 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
     const int64_t c_kv = int64_t(layout->num_sides) * layout->row_bytes;
     if (c_kv > INT32_MAX) return KVM_ERANGE;
     const int64_t dense = int64_t(num_layers) * c_kv;
-    // hit rows: tiles of the fused kernel; miss rows: a merge with no hit part
-    PlanVec<kvm::LayerBatch>& hit = ctx->layer_plan;
-    PlanVec<kvm::SeqBatch>& keys = ctx->key_plan;  // the same records as an unpack call, for the tile order
-    hit.clear();
-    keys.clear();
-    MergePlan miss(c_kv, ctx->merge_plan);
+    // Every record is checked first, and the move unit of the hit rows set.
     uint64_t bits = uint64_t(uintptr_t(pool)) | uint64_t(layout->row_bytes) |
                     uint64_t(layout->block_stride) | uint64_t(layout->side_stride) |
                     uint64_t(layout->layer_stride);
@@ -1113,33 +1108,58 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
         if (s.t_hit + s.t_miss > 0 && !s.out) return KVM_EINVAL;
         const int64_t ts = s.token_stride ? s.token_stride : dense;
         if (ts < dense) return KVM_EINVAL;
-        if (s.t_miss > 0) {
+        if (s.t_hit > 0)
+            bits |= uint64_t(uintptr_t(s.full)) | uint64_t(ts) | uint64_t(uintptr_t(s.out)) |
+                    uint64_t(s.out_stride);
+    }
+    const int unit = move_unit(bits);
+    // Hit rows: tiles of the fused kernel. A request's miss rows go into the
+    // same launch, as its last work items, when their address and stride keep
+    // that unit; otherwise (and for requests with no hit rows) into a merge
+    // with no hit part.
+    PlanVec<kvm::LayerBatch>& hit = ctx->layer_plan;
+    PlanVec<kvm::SeqBatch>& keys = ctx->key_plan;  // the same records as an unpack call, for the tile order
+    hit.clear();
+    keys.clear();
+    MergePlan miss(c_kv, ctx->merge_plan);
+    const int64_t miss_rows = std::max<int64_t>(1, kMergeTileBytes / c_kv);
+    for (int32_t i = 0; i < n; ++i) {
+        const kvm_layer_seq& s = seqs[i];
+        const int64_t ts = s.token_stride ? s.token_stride : dense;
+        const bool fold = s.t_hit > 0 && s.t_miss > 0 &&
+                          ((uint64_t(uintptr_t(s.miss)) | uint64_t(s.miss_stride)) &
+                           uint64_t(unit - 1)) == 0;
+        if (s.t_miss > 0 && !fold) {
             rc = miss.add(nullptr, 0, 0, s.miss, s.miss_stride, s.t_miss,
                           static_cast<char*>(s.out) + s.t_hit * s.out_stride, s.out_stride);
             if (rc != KVM_OK) return rc;
         }
         if (s.t_hit == 0) continue;
         if (hit.empty() || hit.back().n == kvm::kRecsPerLaunch) {
-            hit.add();
+            kvm::LayerBatch& nb = hit.add();
+            nb.miss0[0] = 0;
+            nb.miss_rows = int32_t(miss_rows);
             keys.add();
         }
         kvm::LayerBatch& b = hit.back();
         kvm::SeqBatch& k = keys.back();
         const int64_t tiles = (s.t_hit + layout->block_tokens - 1) / layout->block_tokens;
         if ((b.tile0[b.n] + tiles) * layout->num_sides > kMaxTiles) return KVM_ERANGE;
+        const int64_t mtiles = fold ? (s.t_miss + miss_rows - 1) / miss_rows : 0;
+        if (b.miss0[b.n] + mtiles > kMaxTiles) return KVM_ERANGE;
         b.rec[b.n] = {s.block_table, static_cast<const char*>(s.full), s.t_hit, ts,
-                      static_cast<char*>(s.out), s.out_stride};
+                      static_cast<char*>(s.out), s.out_stride,
+                      fold ? static_cast<const char*>(s.miss) : nullptr, s.miss_stride,
+                      fold ? s.t_miss : 0};
         k.rec[k.n] = {s.block_table, static_cast<const char*>(s.full), s.t_hit, ts};
         b.tile0[b.n + 1] = k.tile0[k.n + 1] = b.tile0[b.n] + tiles;
+        b.miss0[b.n + 1] = b.miss0[b.n] + mtiles;
         ++b.n;
         ++k.n;
-        bits |= uint64_t(uintptr_t(s.full)) | uint64_t(ts) | uint64_t(uintptr_t(s.out)) |
-                uint64_t(s.out_stride);
     }
     if (hit.empty() && miss.batches.empty()) return KVM_OK;
     if (!hit.empty() && !pool) return KVM_EINVAL;
     if (hit.size() > size_t(kOrderSlots)) return KVM_ERANGE;
-    const int unit = move_unit(bits);
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return KVM_EHIP;
@@ -1161,7 +1181,7 @@ int kvm_unpack_merge_layer(kvm_ctx* ctx, const kvm_pool_layout* layout, void* po
     const PoolGeom g = geom_of(layout);
     for (size_t i = 0; i < hit.size(); ++i) {
         hipError_t e = kvm::launch_unpack_merge(unit, g, static_cast<char*>(pool), layer, hit[i],
-                                                orders[i] ? orders[i]->order : nullptr,
+                                                c_kv, orders[i] ? orders[i]->order : nullptr,
                                                 ctx->d_err, ctx->max_wgs, st);
         if (e != hipSuccess) return fail_hip(ctx, e, "k_unpack_merge launch");
         if (orders[i]) {

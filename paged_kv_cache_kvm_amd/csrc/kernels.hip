@@ -467,11 +467,16 @@ __global__ __launch_bounds__(BS) void k_unpack(PoolGeom g, char* __restrict__ po
 // stores before its output stores rather than the two stores of each element
 // in turn (measured on MI355X: +2-4.5 % on 1152- and 1024-byte MLA rows,
 // -1.2 % on Llama's 2 KiB block sides). Two tiles per item: +1.2 % on Llama.
+// The requests' miss rows follow as the launch's last work items (tiles of
+// batch.miss_rows rows copied to the output rows after the hit rows), so that
+// they fill the slots the hit items leave at the end of the launch instead
+// of taking a merge launch of their own.
 template <int U, int BS, int UNR, bool SPLIT, int G>
 __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restrict__ pool,
                                                      int32_t layer, const LayerBatch batch,
                                                      const int32_t* __restrict__ order,
-                                                     FastDiv div_v, unsigned long long* err)
+                                                     FastDiv div_v, FastDiv div_c,
+                                                     unsigned long long* err)
 {
     typedef typename Unit<U>::T V;
     walk_items<G>(batch, 1, g.sides, order, [&](const Item<G>& it) {
@@ -515,6 +520,31 @@ __global__ __launch_bounds__(BS) void k_unpack_merge(PoolGeom g, char* __restric
             }
         }
     });
+    // The miss rows: work items after the hit items, item m one tile of
+    // batch.miss_rows rows of the record whose miss0 range holds m (out rows
+    // from num_tokens on). Element j of a tile: row j / C, unit column j % C
+    // (C = c_kv / U units, div_c), in thread-major order as k_merge.
+    const int64_t nt = batch.tile0[batch.n];
+    const int64_t hit_items = (G == 1 ? nt : (nt + G - 1) / G) * g.sides;
+    const int64_t nm = batch.miss0[batch.n];
+    const int64_t grid = gridDim.x;
+    int64_t i = blockIdx.x;
+    if (i < hit_items) i += (hit_items - i + grid - 1) / grid * grid;
+    for (; i < hit_items + nm; i += grid) {
+        const int64_t m = i - hit_items;
+        const int32_t si = find_record(batch.miss0, batch.n, m);
+        const LayerRec& s = batch.rec[si];
+        const int64_t row0 = (m - batch.miss0[si]) * batch.miss_rows;
+        const uint32_t rows = uint32_t(min(int64_t(batch.miss_rows), s.t_miss - row0));
+        const char* src = s.miss + row0 * s.miss_stride;
+        char* dst = s.out + (s.num_tokens + row0) * s.out_stride;
+        copy_elements<U, BS, UNR, false>(rows * div_c.d, [&](uint32_t j, const char*& sp, char*& dp) {
+            const uint32_t r = fdiv(j, div_c);
+            const uint32_t c = j - r * div_c.d;
+            sp = src + int64_t(r) * s.miss_stride + int64_t(c) * U;
+            dp = dst + int64_t(r) * s.out_stride + int64_t(c) * U;
+        });
+    }
 }
 
 // --------------------------------------------------------------- merge ---
@@ -1403,30 +1433,32 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
 }
 
 hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t layer,
-                               const LayerBatch& b, const int32_t* order,
+                               const LayerBatch& b, int64_t c_kv, const int32_t* order,
                                unsigned long long* err, int32_t max_wgs, hipStream_t st)
 {
     const FastDiv dv = make_fastdiv(uint32_t(g.row_bytes / unit));
+    const FastDiv dc = make_fastdiv(uint32_t(c_kv / unit));
     const int64_t units = int64_t(g.block_tokens) * (g.row_bytes / unit);
     const int64_t nt = b.tile0[b.n];
+    const int64_t nm = b.miss0[b.n];  // miss tiles, after the hit items
     if (unit == 16 && units > kUnpackWideItem) {
         hipLaunchKernelGGL((k_unpack_merge<16, kFusedWideBS, kFusedWideUnroll, true, 1>),
-                           tile_grid(nt * g.sides, max_wgs), dim3(kFusedWideBS), 0, st, g, pool,
-                           layer, b, order, dv, err);
+                           tile_grid(nt * g.sides + nm, max_wgs), dim3(kFusedWideBS), 0, st, g,
+                           pool, layer, b, order, dv, dc, err);
         return hipGetLastError();
     }
     if (unit == 16 && 2 * units > int64_t(kFusedBS) * kFusedUnroll) {
         // a pair of 16-byte-unit tiles that one 768 x 4 pass does not hold
         // (Llama's 32 KiB block sides) keeps 1024 x 4: one pass, +0.4-1.1 %
         hipLaunchKernelGGL((k_unpack_merge<16, kFusedPairBS, kFusedUnroll, false, 2>),
-                           tile_grid((nt + 1) / 2 * g.sides, max_wgs), dim3(kFusedPairBS), 0, st,
-                           g, pool, layer, b, order, dv, err);
+                           tile_grid((nt + 1) / 2 * g.sides + nm, max_wgs), dim3(kFusedPairBS), 0,
+                           st, g, pool, layer, b, order, dv, dc, err);
         return hipGetLastError();
     }
     if (two_tiles(units)) {
-        const dim3 grid = tile_grid((nt + 1) / 2 * g.sides, max_wgs);
+        const dim3 grid = tile_grid((nt + 1) / 2 * g.sides + nm, max_wgs);
 #define KVM_FUSED_BS(U, BS)                                                                 \
-    hipLaunchKernelGGL((k_unpack_merge<U, BS, kFusedUnroll, false, 2>), grid, dim3(BS), 0, st, g, pool, layer, b, order, dv, err)
+    hipLaunchKernelGGL((k_unpack_merge<U, BS, kFusedUnroll, false, 2>), grid, dim3(BS), 0, st, g, pool, layer, b, order, dv, dc, err)
 #define KVM_FUSED(U)                                                                        \
     if (2 * units <= kSmallPairUnits) KVM_FUSED_BS(U, kFusedSmallBS);                       \
     else KVM_FUSED_BS(U, kFusedBS)
@@ -1434,9 +1466,9 @@ hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t 
 #undef KVM_FUSED
 #undef KVM_FUSED_BS
     } else {
-        const dim3 grid = tile_grid(nt * g.sides, max_wgs);
+        const dim3 grid = tile_grid(nt * g.sides + nm, max_wgs);
 #define KVM_FUSED(U)                                                                        \
-    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, false, 1>), grid, dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, err)
+    hipLaunchKernelGGL((k_unpack_merge<U, kFusedBS, kFusedUnroll, false, 1>), grid, dim3(kFusedBS), 0, st, g, pool, layer, b, order, dv, dc, err)
         KVM_UNIT_SWITCH(unit, KVM_FUSED)
 #undef KVM_FUSED
     }

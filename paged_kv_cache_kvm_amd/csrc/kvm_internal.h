@@ -76,8 +76,9 @@ struct MergeBatch {
     MergeRec rec[kRecsPerLaunch];
 };
 
-// One request of the fused unpack + merge (hit rows only; the miss rows go
-// through k_merge).
+// One request of the fused unpack + merge: its hit rows (num_tokens of them,
+// out rows 0 ..), and the miss rows the same launch copies into out rows
+// num_tokens .. (t_miss of them; 0 when they go through k_merge instead).
 struct LayerRec {
     const int32_t* block_table;
     const char* full;
@@ -85,12 +86,19 @@ struct LayerRec {
     int64_t token_stride;
     char* out;
     int64_t out_stride;
+    const char* miss;
+    int64_t miss_stride;
+    int64_t t_miss;
 };
 
+// tile0: the records' first hit tiles; miss0: their first miss tiles (of
+// miss_rows rows each), numbered after the launch's hit work items.
 struct LayerBatch {
     static constexpr bool kHasOut = true;
     int32_t n;
+    int32_t miss_rows;
     int64_t tile0[kRecsPerLaunch + 1];
+    int64_t miss0[kRecsPerLaunch + 1];
     LayerRec rec[kRecsPerLaunch];
 };
 
@@ -117,9 +125,11 @@ hipError_t launch_unpack(int unit, const PoolGeom& g, char* pool, int32_t num_la
                          unsigned long long* err, int32_t max_wgs, hipStream_t st);
 
 // Hit rows of one layer into the pool slots and into the output rows, one
-// read per row; `order` as for launch_unpack (made from the same tables).
+// read per row, then the records' miss rows into their output rows;
+// `order` as for launch_unpack (made from the same tables). c_kv: bytes of
+// one miss row.
 hipError_t launch_unpack_merge(int unit, const PoolGeom& g, char* pool, int32_t layer,
-                               const LayerBatch& b, const int32_t* order,
+                               const LayerBatch& b, int64_t c_kv, const int32_t* order,
                                unsigned long long* err, int32_t max_wgs, hipStream_t st);
 
 // Sort the batch's unpack tiles by destination block id into `order`
