@@ -73,10 +73,15 @@
  *     only once a context has seen two streams (a replaced tile order waits
  *     for the launches that read it), plus kvm_ctx_set_checks' debug mode,
  *     which synchronises the call's own stream.
- *   - HIP graph capture of these calls is not supported: a captured unpack or
- *     fused launch refers to the context's cached tile order, which a later
- *     call with other block tables may overwrite before the graph replays.
- *     kvm_batch_copy_noalloc is the exception (see there).
+ *   - HIP graph capture: kvm_pack_full and kvm_merge_layer may be captured.
+ *     They read no state the context keeps between calls (their records
+ *     travel as kernel arguments), allocate nothing, record no event and
+ *     clear nothing with a memset, so a replay moves the bytes the buffers
+ *     hold then, through the pointers and sizes given at capture. Unpack and
+ *     the fused call may not: their launches read the context's cached tile
+ *     order, which a later call with other block tables may overwrite before
+ *     the graph replays. kvm_batch_copy may not (its scratch and piece counts
+ *     are the context's); kvm_batch_copy_noalloc may (see there).
  *   - Caller preconditions: the block tables of one unpack or fused call
  *     hold no repeated entry; pool rows described by the layout do not overlap;
  *     copy destinations are pairwise disjoint and do not overlap the sources.
