@@ -657,23 +657,33 @@ def mla_section(torch, kv, wl, ctx, dev, seed, reps=5, verify=False):
                                f"back, divided by {L}")
     assert ctx.take_device_errors() == 0
     if verify:
-        # every layer of one more separate loop, each checked right after its moves
+        # every layer of one more separate loop, then of one more fused loop
+        # (its slot pool and complete_layer ring reset to the sentinel first),
+        # each checked right after its moves
         slots = slot.view(N, B, C)
-        for l in range(L):
-            kv.kvm_unpack_layer(ctx.handle, layout, slot, L, l, seqs)
-            kv.kvm_merge_layer(ctx.handle, C, merge_l[l])
+        for l in list(range(L)) + [-1 - l for l in range(L)]:
+            fused_pass = l < 0
+            l = -1 - l if fused_pass else l
             ring = rings[l % 2]
+            if fused_pass:
+                slot.fill_(0xA5)
+                ring.fill_(0xA5)
+                kv.kvm_unpack_merge_layer(ctx.handle, layout, slot, L, l, fused_l[l])
+            else:
+                kv.kvm_unpack_layer(ctx.handle, layout, slot, L, l, seqs)
+                kv.kvm_merge_layer(ctx.handle, C, merge_l[l])
             mbase = l * miss_all
             for r in range(R):
                 th = w.t_hit[r]
                 fbl = fbs[r].view(th, L, C)[:, l]
                 o = ring[roff[r]:roff[r + 1]].view(-1, C)
-                expect(torch.equal(o[:th], fbl), f"mla complete_layer hit rows, layer {l} request {r}")
+                tag = "fused " if fused_pass else ""
+                expect(torch.equal(o[:th], fbl), f"mla {tag}complete_layer hit rows, layer {l} request {r}")
                 expect(torch.equal(o[th:], misses[mbase + moff[r]:mbase + moff[r + 1]].view(-1, C)),
-                       f"mla complete_layer miss rows, layer {l} request {r}")
+                       f"mla {tag}complete_layer miss rows, layer {l} request {r}")
                 t = torch.arange(th, device=slot.device)
                 expect(torch.equal(slots[bts[r].long()[t // B], t % B], fbl),
-                       f"mla slot rows, layer {l} request {r}")
+                       f"mla {tag}slot rows, layer {l} request {r}")
     del fbs, misses, slot, rings, bts
     torch.cuda.empty_cache()
     return out
@@ -1027,6 +1037,20 @@ def main():
                      "GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
     dom = max(ops, key=lambda k: ops[k]["ms_per_launch"] * ops[k]["launches_per_step"])
     fused = fused_section(torch, kv, ctx, s, args.steps, args.warmup, ms_step)
+    if args.verify:
+        def verify_fused():
+            # one more fused step (32 x unpack_merge_layer + pack_full) into
+            # complete_layer and Full Blocks reset to the sentinel, checked as
+            # the separate loop is
+            complete, packed = s["keep"][3], s["keep"][4]
+            complete.fill_(0xA5)
+            for p in packed:
+                p.fill_(0xA5)
+            llama_fused_step(kv, ctx, s)
+            torch.cuda.synchronize()
+            verify_layer_loop(torch, s)
+        run_verify(verify_fused)
+        verified["fused_layer_loop"] = "pass"
     host = None if args.no_host else host_tier_section(torch, kv, ctx, s)
     pipe = None
     if not args.no_pipeline:
