@@ -1040,12 +1040,19 @@ def main():
     if args.verify:
         def verify_fused():
             # one more fused step (32 x unpack_merge_layer + pack_full) into
-            # complete_layer and Full Blocks reset to the sentinel, checked as
-            # the separate loop is
-            complete, packed = s["keep"][3], s["keep"][4]
+            # complete_layer, Full Blocks and the hit tokens' pool slots reset
+            # to the sentinel, checked as the separate loop is
+            bts, complete, packed = s["keep"][0], s["keep"][3], s["keep"][4]
             complete.fill_(0xA5)
             for p in packed:
                 p.fill_(0xA5)
+            sh = s["w"].shape
+            B, th = sh.block_tokens, s["w"].t_hit[0]
+            pv = s["pool"].view(s["L"], sh.sides, s["w"].pool_blocks, B, sh.row_bytes)
+            for bt in bts:
+                for t0 in range(0, th, 4096):
+                    t = torch.arange(t0, min(th, t0 + 4096), device=pv.device)
+                    pv[:, :, bt.long()[t // B], t % B] = 0xA5
             llama_fused_step(kv, ctx, s)
             torch.cuda.synchronize()
             verify_layer_loop(torch, s)
