@@ -427,6 +427,11 @@ FUSED_CASES = [
     (2, 2, 24, 256, 100, [(1000, 30), (257, 0), (3, 5)], "dense", 0, 0, 0, 0),  # 256-token blocks
     (1, 1, 10, 1024, 16, [(3000, 100), (1025, 1)], "slot", 0, 0, 16, 0),     # 1024-token blocks
     (2, 2, 64, 16, 1024, [(300, 20), (77, 3)], "dense", 0, 0, 0, 0),           # 64-wide heads
+    # miss rows in the fused launch, several 64 KiB tiles of them per request
+    # (1 KiB rows), beside a request with miss rows only (its own merge launch)
+    (2, 2, 100, 16, 512, [(300, 200), (0, 70), (50, 130)], "dense", 0, 0, 0, 0),
+    # miss rows 8 bytes off the hit rows' 16-byte unit: a merge launch of their own
+    (2, 2, 100, 16, 512, [(300, 200), (50, 130)], "dense", 0, 8, 0, 0),
 ]
 
 
