@@ -693,6 +693,7 @@ def small_call_section(torch, kv, wl, ctx, dev, calls=2000):
     """Per-call cost of small calls, back to back on one stream with no sync in
     between: the pages' case for batching is the submission cost per object.
     unpack_layer of the tiny workload (one request of 240 hit tokens, 30 KiB),
+    the fused unpack_merge_layer of the same request with its 16 miss tokens,
     a batched copy of 64 objects of 4 KiB, and for reference one torch device
     copy of 4 KiB per call. Microseconds per call on the host clock, pipelined."""
     w = wl.TINY
@@ -705,6 +706,10 @@ def small_call_section(torch, kv, wl, ctx, dev, calls=2000):
     full = torch.empty(t_hit * L * S * rb, **u8)
     layout = kv.pool_layout(S, B, rb, B * rb, N * B * rb, S * N * B * rb, N)
     seqs = [kv.seq(bt, full, t_hit)]
+    t_miss, C = w.t_miss[0], S * rb
+    miss = torch.empty(t_miss * C, **u8)
+    out = torch.empty((t_hit + t_miss) * C, **u8)
+    fused = kv.records([kv.layer_seq(bt, full, t_hit, miss.data_ptr(), C, t_miss, out, C)])
     import numpy as np
     lens = np.full(64, 4096, np.int64)
     d = np.stack([wl.placements(9, 1, lens, 1 << 22), wl.placements(9, 2, lens, 1 << 22), lens],
@@ -737,6 +742,8 @@ def small_call_section(torch, kv, wl, ctx, dev, calls=2000):
                 lambda: lib.kvm_unpack_layer(ctx.handle, lay, pool_p, L, 1, arr, 1, st)), 2),
             "pack_full_tiny_c_us": round(per_call(
                 lambda: lib.kvm_pack_full(ctx.handle, lay, pool_p, L, arr, 1, st)), 2),
+            "unpack_merge_layer_tiny_c_us": round(per_call(
+                lambda: lib.kvm_unpack_merge_layer(ctx.handle, lay, pool_p, L, 1, fused, 1, st)), 2),
             "batch_copy_64x4KiB_us": round(per_call(
                 lambda: kv.kvm_batch_copy(ctx.handle, dst, 1 << 22, src, 1 << 22, descs, 64)), 2),
             "batch_copy_64x4KiB_c_us": round(per_call(
